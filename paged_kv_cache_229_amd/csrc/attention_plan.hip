@@ -1,0 +1,236 @@
+// Device-side work plan and split-context reduction for paged attention.
+//
+// The host never reads context_lens or query_start_loc (that would need a device-to-host sync), so the
+// decomposition into work is made here, on the device, in one small workgroup:
+//
+//   unit = (sequence s, row tile t, context partition p), processed once per kv head.
+//
+// The rows of (s, kv head g) are the pairs (query token i, query head of g's group), row = i * G + h',
+// so a tile holds several tokens' worth of grouped heads and the keys it loads serve all of them.  Row
+// tile t covers rows [t*RT, min(rows, (t+1)*RT)); its last token sees keys [0, kmax).  A tile whose kmax
+// exceeds the partition length P is split into ceil(kmax / P) partitions; P is picked so the whole call
+// has about `target_items` (unit, kv head) items, enough to fill 256 compute units several times over.
+// Each partition of a split tile leaves (acc, m, l) per row; split_reduce_kernel merges them:
+//     M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+// (m in log2 units: the main kernel folds log2(e) into the score scale).
+//
+// The method's softmax is "Paged Attention 基础 – 原理与实现进度", §2 step 5; splitting the key range and
+// merging the partial softmax sums gives the same result up to float32 rounding order.
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ inline bool seq_ok(int q_lo, int q_hi, int context_len, int64_t total_q, int max_context) {
+  return q_lo >= 0 && q_hi >= q_lo && q_hi <= total_q && context_len >= q_hi - q_lo &&
+         context_len <= max_context;
+}
+
+// One past the last key the tile's last row may see.
+__device__ inline int tile_kmax(int context_len, int n, int group, int rows, int rows_per_tile, int t) {
+  const int last_row = min(rows, (t + 1) * rows_per_tile) - 1;
+  return context_len - n + last_row / group + 1;
+}
+
+// Exclusive prefix sum over the workgroup; *total receives the sum of all values.
+__device__ long long block_exclusive_scan(long long v, long long* total, long long* sm) {
+  const int t = threadIdx.x;
+  sm[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const long long x = t >= off ? sm[t - off] : 0;
+    __syncthreads();
+    sm[t] += x;
+    __syncthreads();
+  }
+  const long long incl = sm[t];
+  *total = sm[kPlanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__device__ long long block_max(long long v, long long* sm) {
+  const int t = threadIdx.x;
+  sm[t] = v;
+  __syncthreads();
+  for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
+    if (t < off) sm[t] = max(sm[t], sm[t + off]);
+    __syncthreads();
+  }
+  const long long r = sm[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) {
+  __shared__ long long sm[kPlanThreads];
+  const int t = threadIdx.x;
+  const int N = p.num_seqs;
+  const int per = (N + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(N, t * per);
+  const int s1 = min(N, s0 + per);
+  const int RT = p.rows_per_tile;
+  const int G = p.group;
+  const int* qsl = p.query_start_loc;
+
+  long long work = 0, tiles = 0, bad = 0, maxk = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int lo = qsl[s], hi = qsl[s + 1], L = p.context_lens[s];
+    const int n = hi - lo;
+    int nt = 0;
+    if (!seq_ok(lo, hi, L, p.total_q, p.max_context)) {
+      ++bad;
+    } else if (n > 0) {
+      const int rows = n * G;
+      nt = (rows + RT - 1) / RT;
+      for (int tt = 0; tt < nt; ++tt) {
+        const int km = tile_kmax(L, n, G, rows, RT, tt);
+        work += km;
+        maxk = max(maxk, static_cast<long long>(km));
+      }
+    }
+    p.buf.seq_tiles[s] = nt;
+    tiles += nt;
+  }
+  long long total_work, total_tiles, total_bad;
+  block_exclusive_scan(work, &total_work, sm);
+  block_exclusive_scan(bad, &total_bad, sm);
+  const long long tile_off = block_exclusive_scan(tiles, &total_tiles, sm);
+  const long long max_kmax = block_max(maxk, sm);
+
+  if (total_tiles > p.tile_cap) {  // inconsistent metadata: do nothing
+    if (t == 0) {
+      p.buf.hdr[kHdrUnits] = 0;
+      p.buf.hdr[kHdrQueue] = 0;
+      p.buf.hdr[kHdrPartition] = kStageKeys;
+      p.buf.hdr[kHdrTiles] = 0;
+      p.buf.hdr[kHdrBadSeqs] = -1;
+    }
+    return;
+  }
+
+  long long P;
+  if (p.forced_partition > 0) {
+    P = (p.forced_partition + kStageKeys - 1) / kStageKeys * kStageKeys;
+  } else {
+    const long long items = total_work * p.num_kv_heads;
+    const long long want = (items + p.target_items - 1) / p.target_items;
+    P = (want + kStageKeys - 1) / kStageKeys * kStageKeys;
+    if (P < kMinPartition) P = kMinPartition;
+  }
+
+  long long units_total = 0, unit_off = 0;
+  for (;;) {
+    long long units = 0;
+    for (int s = s0; s < s1; ++s) {
+      const int nt = p.buf.seq_tiles[s];
+      if (nt == 0) continue;
+      const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
+      const int rows = n * G;
+      for (int tt = 0; tt < nt; ++tt) units += (tile_kmax(L, n, G, rows, RT, tt) + P - 1) / P;
+    }
+    unit_off = block_exclusive_scan(units, &units_total, sm);
+    if (units_total <= p.unit_cap || P >= max_kmax) break;
+    P *= 2;
+  }
+
+  long long tb = tile_off, ub = unit_off;
+  for (int s = s0; s < s1; ++s) {
+    p.buf.tile_base[s] = static_cast<int>(tb);
+    const int nt = p.buf.seq_tiles[s];
+    if (nt == 0) continue;
+    const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
+    const int rows = n * G;
+    for (int tt = 0; tt < nt; ++tt) {
+      const int np = static_cast<int>((tile_kmax(L, n, G, rows, RT, tt) + P - 1) / P);
+      p.buf.tile_rec[tb] = make_int2(static_cast<int>(ub), np);
+      ++tb;
+      for (int pp = 0; pp < np; ++pp) p.buf.units[ub++] = make_int4(s, tt, pp, np);
+    }
+  }
+  if (t == 0) {
+    p.buf.tile_base[N] = static_cast<int>(total_tiles);
+    p.buf.hdr[kHdrUnits] = static_cast<int>(units_total);
+    p.buf.hdr[kHdrQueue] = 0;
+    p.buf.hdr[kHdrPartition] = static_cast<int>(P);
+    p.buf.hdr[kHdrTiles] = static_cast<int>(total_tiles);
+    p.buf.hdr[kHdrBadSeqs] = static_cast<int>(total_bad);
+  }
+}
+
+// One workgroup per (row tile, kv head).  Tiles with a single partition were finished by the main
+// kernel and are skipped.
+template <int D>
+__global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams p) {
+  const int tile_idx = blockIdx.x;
+  const int g = blockIdx.y;
+  if (tile_idx >= p.buf.hdr[kHdrTiles]) return;
+  const int2 rec = p.buf.tile_rec[tile_idx];
+  if (rec.y <= 1) return;
+  const int4 u = p.buf.units[rec.x];
+  const int s = u.x, tile = u.y;
+  const int q0 = p.query_start_loc[s];
+  const int n = p.query_start_loc[s + 1] - q0;
+  const int G = p.group;
+  const int RT = p.rows_per_tile;
+  const int row0 = tile * RT;
+  const int rows_here = min(RT, n * G - row0);
+  constexpr int D4 = D / 4;
+  for (int w = threadIdx.x; w < rows_here * D4; w += kThreads) {
+    const int rl = w / D4;
+    const int d0 = (w - rl * D4) * 4;
+    float M = -INFINITY;
+    for (int pp = 0; pp < rec.y; ++pp) {
+      const int64_t item = static_cast<int64_t>(rec.x + pp) * p.num_kv_heads + g;
+      M = fmaxf(M, p.buf.part_ml[item * RT + rl].x);
+    }
+    const float mref = M == -INFINITY ? 0.f : M;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, den = 0.f;
+    for (int pp = 0; pp < rec.y; ++pp) {
+      const int64_t item = static_cast<int64_t>(rec.x + pp) * p.num_kv_heads + g;
+      const float2 ml = p.buf.part_ml[item * RT + rl];
+      const float wgt = __builtin_amdgcn_exp2f(ml.x - mref);
+      den += wgt * ml.y;
+      const float4 a = *reinterpret_cast<const float4*>(p.buf.part_acc + (item * RT + rl) * D + d0);
+      a0 += wgt * a.x;
+      a1 += wgt * a.y;
+      a2 += wgt * a.z;
+      a3 += wgt * a.w;
+    }
+    const float inv = 1.f / den;
+    const int r = row0 + rl;
+    const int i = r / G;
+    const int hh = r - i * G;
+    __bf16* o = static_cast<__bf16*>(p.out) +
+                ((static_cast<int64_t>(q0 + i) * p.num_q_heads + g * G + hh) * D + d0);
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v;
+    v[0] = static_cast<__bf16>(a0 * inv);
+    v[1] = static_cast<__bf16>(a1 * inv);
+    v[2] = static_cast<__bf16>(a2 * inv);
+    v[3] = static_cast<__bf16>(a3 * inv);
+    *reinterpret_cast<bf16x4*>(o) = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream) {
+  if (tile_cap <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tile_cap), static_cast<unsigned>(p.num_kv_heads));
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(split_reduce_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

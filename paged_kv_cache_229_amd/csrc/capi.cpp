@@ -1,0 +1,321 @@
+// C-ABI entry points: host-side argument checks, workspace layout and kernel launches.
+//
+// Every check runs on the host before the first HIP call, so an invalid call never enqueues anything and
+// can be exercised without a GPU.  Nothing here reads device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "kernels.h"
+#include "paged_kv.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+thread_local std::string g_error;
+thread_local int g_partition_keys = 0;
+thread_local int g_target_items = 0;
+thread_local int g_tile_kind = 0;
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+int fail(int status, const std::string& msg) {
+  g_error = msg;
+  return status;
+}
+
+int succeed() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int r = 0;
+  while ((int64_t{1} << r) < x) ++r;
+  return r;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+// Checks shared by both operations: element type, head_dim, block_size, heads, pool geometry.
+int check_pool(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_kv_heads,
+               int64_t num_blocks, int64_t block_stride, int64_t* stride_out) {
+  if (dtype != PKV_FP32 && dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype must be PKV_FP32 (0) or PKV_BF16 (1)");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got " + std::to_string(head_dim));
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "block_size must be a power of two in [8, 256], got " + std::to_string(block_size));
+  if (num_kv_heads < 1) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (num_blocks > (int64_t{INT32_MAX} / block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "num_blocks * block_size must be < 2^31");
+  const int64_t dense = static_cast<int64_t>(block_size) * num_kv_heads * head_dim;
+  if (block_stride == 0) block_stride = dense;
+  if (block_stride < dense)
+    return fail(PKV_ERR_INVALID_ARG, "block_stride is smaller than block_size * num_kv_heads * head_dim");
+  if ((block_stride * elem_bytes(dtype)) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "block_stride * element size must be a multiple of 16 bytes");
+  *stride_out = block_stride;
+  return PKV_OK;
+}
+
+struct WsLayout {
+  size_t hdr, seq_tiles, seq_units, tile_base, tile_rec, units, part_ml, part_acc, total;
+  int rows_per_tile;
+  int64_t tile_cap, unit_cap;
+};
+
+int choose_tile_kind(int group, int64_t total_q, int32_t max_q_len_hint) {
+  if (g_tile_kind == 1 || g_tile_kind == 2) return g_tile_kind;
+  (void)group;
+  (void)total_q;
+  (void)max_q_len_hint;
+  return 1;
+}
+
+WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int tile_kind) {
+  WsLayout w{};
+  const int group = num_q_heads / num_kv_heads;
+  w.rows_per_tile = tile_kind == 2 ? 128 : 64;
+  // Each sequence adds at most one partly filled tile.
+  w.tile_cap = (total_q * group + w.rows_per_tile - 1) / w.rows_per_tile + num_seqs;
+  w.unit_cap = (pkv::kMaxItems + num_kv_heads - 1) / num_kv_heads + w.tile_cap;
+  size_t off = 0;
+  w.hdr = off;
+  off = round256(off + 16 * sizeof(int));
+  w.seq_tiles = off;
+  off = round256(off + static_cast<size_t>(num_seqs) * sizeof(int));
+  w.seq_units = off;
+  off = round256(off + static_cast<size_t>(num_seqs) * sizeof(int));
+  w.tile_base = off;
+  off = round256(off + static_cast<size_t>(num_seqs + 1) * sizeof(int));
+  w.tile_rec = off;
+  off = round256(off + static_cast<size_t>(w.tile_cap) * 2 * sizeof(int));
+  w.units = off;
+  off = round256(off + static_cast<size_t>(w.unit_cap) * 4 * sizeof(int));
+  const size_t part_rows = static_cast<size_t>(w.unit_cap) * num_kv_heads * w.rows_per_tile;
+  w.part_ml = off;
+  off = round256(off + part_rows * 2 * sizeof(float));
+  w.part_acc = off;
+  off = round256(off + part_rows * head_dim * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
+int hip_fail(const char* what, hipError_t e) {
+  return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_abi_version(void) { return kAbiVersion; }
+
+const char* paged_kv_last_error(void) { return g_error.c_str(); }
+
+int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int64_t num_tokens,
+                   void* k_cache, void* v_cache, int64_t num_blocks, int32_t block_size,
+                   int64_t block_stride, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  int64_t stride = 0;
+  const int rc = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
+  if (rc != PKV_OK) return rc;
+  if (num_tokens == 0) return succeed();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer among k, v, slot_mapping, k_cache, v_cache");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 4))
+    return fail(PKV_ERR_INVALID_ARG, "k, v, k_cache, v_cache must be 16-byte aligned");
+  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * elem_bytes(dtype);
+  const int64_t cpr = row_bytes / 16;
+  if (num_tokens * 2 * cpr > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "num_tokens * row size too large for one call; split the write");
+  pkv::KvWriteParams p{};
+  p.k = k;
+  p.v = v;
+  p.slot_mapping = slot_mapping;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.num_tokens = static_cast<int>(num_tokens);
+  p.chunks_per_row = static_cast<int>(cpr);
+  p.block_size_log2 = log2i(block_size);
+  p.num_slots = num_blocks * block_size;
+  p.block_stride_bytes = stride * elem_bytes(dtype);
+  const hipError_t e = pkv::launch_kv_write(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("paged_kv_write launch", e);
+  return succeed();
+}
+
+size_t paged_attention_workspace_size(int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                      int32_t max_q_len_hint) {
+  if (num_seqs < 0 || total_q < 0 || num_kv_heads < 1 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) ||
+      (dtype != PKV_FP32 && dtype != PKV_BF16)) {
+    fail(PKV_ERR_INVALID_ARG, "invalid sizes for paged_attention_workspace_size");
+    return 0;
+  }
+  g_error.clear();
+  if (dtype == PKV_FP32 || num_seqs == 0 || total_q == 0) return 0;
+  const int group = num_q_heads / num_kv_heads;
+  return workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                          choose_tile_kind(group, total_q, max_q_len_hint))
+      .total;
+}
+
+int paged_attention_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* query_start_loc,
+                            int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
+                            int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (num_seqs < 0 || total_q < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs and total_q must be >= 0");
+  int64_t stride = 0;
+  const int rc = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
+  if (rc != PKV_OK) return rc;
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size must be < 2^31");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  const int group = num_q_heads / num_kv_heads;
+  if (total_q * group > INT32_MAX / 2 || total_q * num_q_heads > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "total_q too large for one call");
+  if (num_seqs == 0 || total_q == 0) return succeed();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return fail(PKV_ERR_INVALID_ARG,
+                "null pointer among out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PKV_ERR_INVALID_ARG, "out, q, k_cache, v_cache must be 16-byte aligned");
+
+  pkv::AttnParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start_loc = query_start_loc;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.block_size_log2 = log2i(block_size);
+  p.num_blocks = num_blocks;
+  p.block_stride = stride;
+  p.total_q = total_q;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool timed = g_ev_start != nullptr && g_ev_stop != nullptr;
+
+  if (dtype == PKV_FP32) {
+    if (timed) hipEventRecord(g_ev_start, st);
+    hipError_t e = pkv::launch_attention_fp32(p, head_dim, st);
+    if (e != hipSuccess) return hip_fail("fp32 attention launch", e);
+    if (timed) hipEventRecord(g_ev_stop, st);
+    return succeed();
+  }
+
+  const int tile_kind = choose_tile_kind(group, total_q, max_q_len_hint);
+  const WsLayout w = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(w.total) + " bytes, got " +
+                                       std::to_string(workspace_bytes));
+  if (!aligned(workspace, 256)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  pkv::PlanBuffers b{};
+  b.hdr = reinterpret_cast<int*>(ws + w.hdr);
+  b.seq_tiles = reinterpret_cast<int*>(ws + w.seq_tiles);
+  b.seq_units = reinterpret_cast<int*>(ws + w.seq_units);
+  b.tile_base = reinterpret_cast<int*>(ws + w.tile_base);
+  b.tile_rec = reinterpret_cast<int2*>(ws + w.tile_rec);
+  b.units = reinterpret_cast<int4*>(ws + w.units);
+  b.part_ml = reinterpret_cast<float2*>(ws + w.part_ml);
+  b.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
+  p.buf = b;
+  p.rows_per_tile = w.rows_per_tile;
+
+  pkv::PlanParams pp{};
+  pp.context_lens = context_lens;
+  pp.query_start_loc = query_start_loc;
+  pp.num_seqs = num_seqs;
+  pp.total_q = total_q;
+  pp.group = group;
+  pp.num_kv_heads = num_kv_heads;
+  pp.rows_per_tile = w.rows_per_tile;
+  pp.max_context = max_blocks_per_seq * block_size;
+  int items = g_target_items > 0 ? g_target_items : pkv::kDefaultItems;
+  if (items > pkv::kMaxItems) items = pkv::kMaxItems;
+  pp.target_items = items;
+  pp.forced_partition = g_partition_keys;
+  pp.unit_cap = static_cast<int>(w.unit_cap);
+  pp.tile_cap = static_cast<int>(w.tile_cap);
+  pp.buf = b;
+
+  hipError_t e = pkv::launch_plan(pp, st);
+  if (e != hipSuccess) return hip_fail("plan launch", e);
+  int64_t grid = static_cast<int64_t>(num_cus()) * pkv::attention_bf16_wgs_per_cu(head_dim, tile_kind);
+  const int64_t max_items = w.unit_cap * num_kv_heads;
+  if (grid > max_items) grid = max_items;
+  if (timed) hipEventRecord(g_ev_start, st);
+  e = pkv::launch_attention_bf16(p, head_dim, tile_kind, static_cast<int>(grid), st);
+  if (e != hipSuccess) return hip_fail("attention launch", e);
+  if (timed) hipEventRecord(g_ev_stop, st);
+  e = pkv::launch_split_reduce(p, head_dim, static_cast<int>(w.tile_cap), st);
+  if (e != hipSuccess) return hip_fail("split reduce launch", e);
+  return succeed();
+}
+
+int paged_attention_set_tuning(int32_t partition_keys, int32_t target_items, int32_t tile_kind) {
+  if (partition_keys < 0 || target_items < 0 || tile_kind < 0 || tile_kind > 2)
+    return fail(PKV_ERR_INVALID_ARG, "tuning values must be >= 0 and tile_kind in {0, 1, 2}");
+  if (target_items > pkv::kMaxItems)
+    return fail(PKV_ERR_INVALID_ARG, "target_items must be <= " + std::to_string(pkv::kMaxItems));
+  g_partition_keys = partition_keys;
+  g_target_items = target_items;
+  g_tile_kind = tile_kind;
+  return succeed();
+}
+
+int paged_attention_set_profile_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "pass both events or neither");
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
+  return succeed();
+}
+
+}  // extern "C"

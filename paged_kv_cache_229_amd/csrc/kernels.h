@@ -1,0 +1,95 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Keys staged in LDS per step of the attention main loop: 4 waves x 32 keys.
+constexpr int kStageKeys = 128;
+constexpr int kThreads = 256;
+// Upper bound on the automatic work-item target (items = units x kv heads).
+constexpr int kMaxItems = 4096;
+constexpr int kDefaultItems = 1024;
+constexpr int kMinPartition = 256;
+
+// Workspace header words.
+enum HeaderWord { kHdrUnits = 0, kHdrQueue = 1, kHdrPartition = 2, kHdrTiles = 3, kHdrBadSeqs = 4 };
+
+// Device work plan, all in the caller's workspace.  A unit is (sequence, row tile, context partition);
+// every unit is processed once per kv head.
+struct PlanBuffers {
+  int* hdr;         // [16]
+  int* seq_tiles;   // [num_seqs]  scratch
+  int* seq_units;   // [num_seqs]  scratch
+  int* tile_base;   // [num_seqs + 1] first tile record of each sequence
+  int2* tile_rec;   // [tile_cap]  {first unit, number of partitions}
+  int4* units;      // [unit_cap]  {sequence, tile, partition, partitions of the tile}
+  float2* part_ml;  // [unit_cap * H_kv * rows_per_tile]  running max (log2 units) and sum per row
+  float* part_acc;  // [unit_cap * H_kv * rows_per_tile * head_dim] unnormalised partial outputs
+};
+
+struct PlanParams {
+  const int* context_lens;
+  const int* query_start_loc;
+  int num_seqs;
+  int64_t total_q;
+  int group;          // num_q_heads / num_kv_heads
+  int num_kv_heads;
+  int rows_per_tile;
+  int max_context;    // max_blocks_per_seq * block_size: longer contexts are rejected on the device
+  int target_items;
+  int forced_partition;
+  int unit_cap;
+  int tile_cap;
+  PlanBuffers buf;
+};
+
+struct AttnParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int* block_tables;
+  const int* context_lens;
+  const int* query_start_loc;
+  int max_blocks_per_seq;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int block_size_log2;
+  int rows_per_tile;
+  int64_t num_blocks;
+  int64_t block_stride;  // elements
+  int64_t total_q;
+  float scale;           // natural-exponent scale
+  float scale_log2;      // scale * log2(e)
+  PlanBuffers buf;
+};
+
+struct KvWriteParams {
+  const void* k;
+  const void* v;
+  const int* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int num_tokens;
+  int chunks_per_row;       // 16-byte chunks in one token row (H_kv * D * elem / 16)
+  int block_size_log2;
+  int64_t num_slots;        // num_blocks * block_size
+  int64_t block_stride_bytes;
+};
+
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+// tile_kind 1: 64-row tiles, 2: 128-row tiles.  grid = persistent workgroups.
+hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
+                                 hipStream_t stream);
+hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream);
+hipError_t launch_attention_fp32(const AttnParams& p, int head_dim, hipStream_t stream);
+// Workgroups per CU the bf16 attention kernel is built for (from its LDS footprint).
+int attention_bf16_wgs_per_cu(int head_dim, int tile_kind);
+
+}  // namespace pkv

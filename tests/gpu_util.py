@@ -1,0 +1,83 @@
+"""Helpers shared by the GPU tests: moving seeded workloads to the device, running one step through the
+C-ABI binding, and comparing with the oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_229_amd as pkv
+from workloads import BF16
+
+
+def dev() -> torch.device:
+    return torch.device("cuda", 0)
+
+
+def to_torch(a: np.ndarray, dtype: str | None, device=None) -> torch.Tensor:
+    """numpy input -> device tensor; bf16 arrays are uint16 bit patterns."""
+    device = device or dev()
+    if dtype == BF16 and a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def pool_bits(t: torch.Tensor) -> np.ndarray:
+    """Device pool -> host array of raw bits (uint16 for bf16, uint32 for fp32)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint32)
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class DeviceWorkload:
+    """A workload's inputs on the GPU (pools copied once; metadata per step)."""
+
+    def __init__(self, w, pools: bool = True):
+        self.w = w
+        self.k_pool = to_torch(w.k_pool, w.dtype) if pools else None
+        self.v_pool = to_torch(w.v_pool, w.dtype) if pools else None
+        self.block_tables = to_torch(w.block_tables, None)
+        self.steps = []
+        for st in w.steps:
+            self.steps.append(dict(
+                q=to_torch(st.q, w.dtype), k_new=to_torch(st.k_new, w.dtype),
+                v_new=to_torch(st.v_new, w.dtype), slot_mapping=to_torch(st.slot_mapping, None),
+                context_lens=to_torch(st.context_lens, None),
+                query_start_loc=to_torch(st.query_start_loc, None),
+                max_q_len=int(np.max(np.diff(st.query_start_loc), initial=0))))
+
+    def run_step(self, i: int, k_pool=None, v_pool=None, block_tables=None, out=None) -> torch.Tensor:
+        s = self.steps[i]
+        kp = self.k_pool if k_pool is None else k_pool
+        vp = self.v_pool if v_pool is None else v_pool
+        bt = self.block_tables if block_tables is None else block_tables
+        pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], kp, vp)
+        return pkv.paged_attention_forward(s["q"], kp, vp, bt, s["context_lens"], s["query_start_loc"],
+                                           scale=self.w.scale, out=out, max_q_len=s["max_q_len"])
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> dict:
+    """bf16: max-abs <= 2e-2 and mean-abs <= 2e-3; fp32: max-abs <= 1e-5 (against the fp64 oracle)."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    stats = dict(max_abs=float(err.max(initial=0.0)), mean_abs=float(err.mean()) if err.size else 0.0,
+                 rms_rel=float(np.sqrt(np.mean(err ** 2)) / max(1e-30, np.sqrt(np.mean(ref ** 2))))
+                 if err.size else 0.0)
+    log(f"{what}: {stats}")
+    if dtype == BF16:
+        assert stats["max_abs"] <= 2e-2 and stats["mean_abs"] <= 2e-3, (what, stats)
+    else:
+        assert stats["max_abs"] <= 1e-5, (what, stats)
+    return stats
