@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = paged_kv_write of the step's new K/V + paged_attention_forward, on one GPU.
+
+    python bench.py [--workload decode|mixed|spec|prefix] [--steps K] [--warmup W] [--gpus 1]
+
+Prints ONE JSON line.  Inputs are seeded synthetic workloads (workloads/), resident in HBM before the
+timed region.  The timed region runs exactly K steps between device synchronisations; each step uses the
+next of several pool copies so the K/V stream comes from HBM, not from a cache warmed by the last step.
+The attention kernel's own duration is read from HIP events the library records around it, and gives
+the roofline fraction (algorithmic bytes per launch / average launch time vs 8 TB/s).  The CPU oracle is
+timed on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16, 256 CU x 2.4 GHz x 4096 flop/clk
+METRIC = "paged decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), tokens/s"
+
+
+def algorithmic_work(w) -> dict:
+    """Bytes and flops the step must move/compute at minimum: tokens (not whole blocks) of K and V,
+    Q read and O written once, block-table entries; causal (query, key) pairs only.  Shared prefix
+    blocks count once for "unique" bytes and per sequence for "logical" bytes."""
+    import numpy as np
+    st = w.steps[0]
+    e = w.elem_bytes
+    L = st.context_lens.astype(np.int64)
+    n = np.diff(st.query_start_loc).astype(np.int64)
+    hq, hkv, d, bs = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    row = hkv * d * e
+    kv_logical = int(2 * row * L.sum())
+    shared_tokens = w.shared_prefix_blocks * bs
+    kv_unique = kv_logical - int(2 * row * shared_tokens * max(0, w.num_seqs - 1))
+    total_q = int(n.sum())
+    qo = 2 * total_q * hq * d * e
+    tables = int(4 * (-(-L // bs)).sum())
+    pairs = int(np.sum(n * (L - n) + n * (n + 1) // 2))
+    flops = 4 * d * hq * pairs
+    write_bytes = 2 * 2 * int(np.count_nonzero(st.slot_mapping >= 0)) * row
+    # prefill subset (sequences with more than one new token) for the mixed workload
+    pre = n > 1
+    pairs_pre = int(np.sum(n[pre] * (L[pre] - n[pre]) + n[pre] * (n[pre] + 1) // 2))
+    return dict(attn_bytes_unique=kv_unique + qo + tables, attn_bytes_logical=kv_logical + qo + tables,
+                write_bytes=write_bytes, flops=flops, total_q=total_q, pairs=pairs,
+                prefill_flops=4 * d * hq * pairs_pre)
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.rt.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self.rt.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        rc = self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, ev: int) -> None:
+        self.rt.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def cpu_baseline(w, work, budget_s: float) -> dict:
+    """The oracle as it stands, on the host cores, over the first sequences of the workload until about
+    ``budget_s`` seconds of work (at least one sequence).  Reported in the same GB/s unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    st = w.steps[0]
+    qsl = st.query_start_loc
+    L = st.context_lens.astype(np.int64)
+    t0 = time.perf_counter()
+    k2, v2 = oracle.kv_write(w.k_pool, w.v_pool, st.k_new, st.v_new, st.slot_mapping)
+    t_write = time.perf_counter() - t0
+    done = []
+    t_attn = 0.0
+    for s in range(w.num_seqs):
+        t1 = time.perf_counter()
+        oracle.paged_attention(st.q, k2, v2, w.block_tables, st.context_lens, qsl, w.scale, w.dtype,
+                               seqs=[s])
+        t_attn += time.perf_counter() - t1
+        done.append(s)
+        if t_write + t_attn >= budget_s:
+            break
+    e = w.elem_bytes
+    row = w.num_kv_heads * w.head_dim * e
+    n = np.diff(qsl).astype(np.int64)
+    sel = np.array(done)
+    bytes_attn = int(2 * row * L[sel].sum() + 2 * n[sel].sum() * w.num_q_heads * w.head_dim * e)
+    bytes_total = bytes_attn + work["write_bytes"]
+    secs = t_write + t_attn
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(bytes_total / secs / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle: the whole step's K/V write plus attention for the first "
+                      f"{len(done)} of {w.num_seqs} sequences ({secs:.1f} s, {os.cpu_count()} host cores "
+                      f"visible, BLAS threads {threads})"}
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["decode", "mixed", "spec", "prefix"])
+    ap.add_argument("--copies", type=int, default=4, help="pool copies rotated across steps")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--items", type=int, default=0)
+    ap.add_argument("--tile-kind", type=int, default=0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_229_amd as pkv
+    from workloads import make_config
+
+    dev = torch.device("cuda", 0)
+    t_gen = time.perf_counter()
+    w = make_config(args.workload, "full")
+    print(f"[bench] generated {w.description} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+    work = algorithmic_work(w)
+    st = w.steps[0]
+
+    def t(a, is_data=True):
+        if is_data and a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    k0, v0 = t(w.k_pool), t(w.v_pool)
+    copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(0, args.copies - 1))]
+    bt = t(w.block_tables, False)
+    q, kn, vn = t(st.q), t(st.k_new), t(st.v_new)
+    sm, cl, qsl = t(st.slot_mapping, False), t(st.context_lens, False), t(st.query_start_loc, False)
+    max_q = int(np.diff(st.query_start_loc).max())
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, pkv.workspace_size(w.num_seqs, q.shape[0], w.num_q_heads,
+                                                 w.num_kv_heads, w.head_dim, q.dtype, max_q)),
+                     dtype=torch.uint8, device=dev)
+    pkv.set_tuning(args.partition, args.items, args.tile_kind)
+
+    def step(i):
+        kp, vp = copies[i % len(copies)]
+        pkv.paged_kv_write(kn, vn, sm, kp, vp)
+        pkv.paged_attention_forward(q, kp, vp, bt, cl, qsl, scale=w.scale, out=out, workspace=ws,
+                                    max_q_len=max_q)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pkv.set_profile_events(*pairs[i])
+        step(args.warmup + i)
+    pkv.set_profile_events(None, None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    ms_step = elapsed * 1e3 / args.steps
+    k_avg = float(np.mean(kernel_ms))
+    step_bytes = work["attn_bytes_unique"] + work["write_bytes"]
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = work["attn_bytes_unique"] / (k_avg * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "num_seqs": w.num_seqs,
+                   "total_q": work["total_q"], "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "pool_copies": len(copies)},
+        "tokens_per_s": round(work["total_q"] / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "attention_kernel_ms": {"mean": round(k_avg, 5), "p10": round(float(np.percentile(kernel_ms, 10)), 5),
+                                "p90": round(float(np.percentile(kernel_ms, 90)), 5)},
+        "attention_tflops": round(work["flops"] / (k_avg * 1e-3) / 1e12, 2),
+        "attention_logical_gbs": round(work["attn_bytes_logical"] / (k_avg * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel",
+                     "bytes_per_launch": work["attn_bytes_unique"]},
+    }
+    if work["prefill_flops"]:
+        result["prefill_subset_flops"] = work["prefill_flops"]
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, work, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
