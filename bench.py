@@ -138,6 +138,8 @@ def main() -> None:
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--items", type=int, default=0)
     ap.add_argument("--tile-kind", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -152,6 +154,15 @@ def main() -> None:
     from workloads import make_config
 
     dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": max(1, args.steps)}), flush=True)
+        return
     t_gen = time.perf_counter()
     w = make_config(args.workload, "full")
     print(f"[bench] generated {w.description} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,

@@ -150,29 +150,32 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p)
     const int nst = (ke - kb + kStageKeys - 1) / kStageKeys;
     u32x4 kreg[T::NLOAD], vreg[T::NLOAD];
 
-    // Wave w loads keys [32w, 32w+32) of stage st.  Rows past ke are not read and become zero.
-    auto issue = [&](int st) {
+    // Block-table entries for one stage: lane i (< NLOAD) fetches the physical block of this wave's
+    // i-th wave-wide load.  Fetched a stage ahead so the data loads never wait on a table lookup.
+    auto fetch_table = [&](int st) -> int {
+      const int i = lane < T::NLOAD ? lane : T::NLOAD - 1;
+      const int kk0 = min(kb + st * kStageKeys + 32 * wave + T::KPL * i, ke - 1);
+      return tbl[kk0 >> bs_log2];
+    };
+    // Wave w loads keys [32w, 32w+32) of stage st.  Keys at or past ke are clamped to row ke-1 of the
+    // same block (a wave-wide load never spans two blocks); their scores are masked, so the duplicate
+    // rows carry probability 0 and rows past the context are never read.
+    auto issue = [&](int st, int tv) {
       const int kbase = kb + st * kStageKeys + 32 * wave;
 #pragma unroll
       for (int i = 0; i < T::NLOAD; ++i) {
-        const int kk0 = kbase + T::KPL * i;
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (kk0 < ke) {
-          const int phys = min(max(tbl[kk0 >> bs_log2], 0), last_block);
-          const int kk = kk0 + lane / T::CPK;
-          if (kk < ke) {
-            const int64_t e = static_cast<int64_t>(phys) * p.block_stride +
-                              (static_cast<int64_t>(kk & bs_mask) * Hkv + g) * D + (lane % T::CPK) * 8;
-            kv = *reinterpret_cast<const u32x4*>(kc + e);
-            vv = *reinterpret_cast<const u32x4*>(vc + e);
-          }
-        }
-        kreg[i] = kv;
-        vreg[i] = vv;
+        const int phys = min(max(__builtin_amdgcn_readlane(tv, i), 0), last_block);
+        const int kk = min(kbase + T::KPL * i + lane / T::CPK, ke - 1);
+        const int64_t e = static_cast<int64_t>(phys) * p.block_stride +
+                          (static_cast<int64_t>(kk & bs_mask) * Hkv + g) * D + (lane % T::CPK) * 8;
+        kreg[i] = *reinterpret_cast<const u32x4*>(kc + e);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vc + e);
       }
     };
 
-    issue(0);
+    int tv = fetch_table(0);
+    issue(0, tv);
+    if (nst > 1) tv = fetch_table(1);
     for (int st = 0; st < nst; ++st) {
       __syncthreads();  // every wave is done reading the previous stage
 #pragma unroll
@@ -193,7 +196,10 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p)
         }
       }
       __syncthreads();
-      if (st + 1 < nst) issue(st + 1);
+      if (st + 1 < nst) {
+        issue(st + 1, tv);
+        if (st + 2 < nst) tv = fetch_table(st + 2);
+      }
 
       const int kstage = kb + st * kStageKeys;
 #pragma unroll
