@@ -12,18 +12,22 @@
 //  * Work item = (unit, kv head) from the device plan; a persistent grid pops items from a queue.  The
 //    rows of an item are (query token, head of g's group) pairs, so all G heads sharing kv head g read
 //    each K/V byte once.
-//  * K/V stream through LDS 128 keys at a time.  Each of the 4 waves loads 32 keys with 16-byte lanes,
-//    one uniform block-table lookup per wave-wide load (a wave-wide load never crosses a block since
-//    block_size >= keys per load), so every load instruction reads whole 256-byte (D=128) rows.  The next
-//    128 keys are loaded into registers while the current ones are used.
-//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16 (keys as M, rows as N):
-//    each lane then owns one row (lane % 16) for every key it holds, so row max / row sum need only two
-//    cross-lane exchanges, and the probabilities already sit in the B-operand layout of O^T = V^T P^T.
-//    The 32 keys of one PV step are taken in the order the S^T fragments deliver them; V is written to
-//    LDS transposed in that same order, so each V^T operand is one 16-byte LDS read.
+//  * K/V stream HBM -> LDS with global_load_lds (no register staging) into a 4-deep ring of 64-key
+//    stages: while one stage is consumed, up to three are in flight.  Each wave fetches 16 keys of a
+//    stage, one uniform physical block per wave-wide load (block_size >= keys per load), each load
+//    instruction covering whole 256-byte (D=128) rows.  Block-table entries come through scalar loads
+//    issued a stage ahead, so the data loads never wait on a lookup.
+//  * In LDS both tiles are row-major [key][D] with the 16-byte chunks of row k XOR-swizzled by k, which
+//    keeps the fragment reads conflict-free.  The swizzle is applied on the way in by choosing which lane
+//    loads which chunk (the DMA writes lane l's 16 bytes at offset 16*l).
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16 (16 keys as M, 16 rows
+//    as N): each lane owns one row (lane % 16) for the 4 keys it holds, so row max and row sum need two
+//    cross-lane exchanges, and the probabilities already sit in the B-operand layout of
+//    O^T += V^T P^T (v_mfma_f32_16x16x16_bf16, 16 keys as K).  The V^T operand (4 keys of one channel per
+//    lane) is read from the row-major V tile with ds_read_b64_tr_b16, one read per MFMA.
 //  * Online softmax in log2 units (scale * log2 e folded into the score scale), exp2 on the VALU.
-//  * Waves split a tile's rows when it has many (prefill), or the keys when it has few (decode); in the
-//    latter case the waves' partial softmax states are merged through LDS at the end.
+//  * Waves split a tile's rows when it has many (prefill, speculative decode), or the keys when it has
+//    few (decode); in the latter case the waves' softmax states are merged through LDS at the end.
 //  * A tile whose context was split into partitions writes (acc, m, l) per row; split_reduce_kernel
 //    merges them.  Unsplit tiles write the normalised bf16 output directly.
 #include "kernels.h"
@@ -31,46 +35,75 @@
 namespace pkv {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
+#define CONST_AS __attribute__((address_space(4)))
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ inline f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ inline f32x4 mfma_pv(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
-// 16-byte-chunk swizzles that keep the fragment reads of both LDS tiles free of bank conflicts.
+// 16-byte HBM -> LDS copy per lane: lane l's 16 bytes from `src` land at LDS byte address
+// lds_base + 16*l (lds_base uniform).  Issued as inline assembly so that the compiler's wait-count pass
+// does not treat every later LDS read as dependent on it (it cannot tell ring slots apart and would drain
+// all loads in flight); readiness of a slot is established explicitly with wait_vmem + a barrier.
+__device__ inline void dma16(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// s_waitcnt on the vector-memory counter only: at most N vector memory operations still outstanding.
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16-byte-chunk swizzle of LDS row `key`.
 template <int D>
 __device__ inline int k_swizzle(int key) {
   return D == 128 ? (key & 15) : ((key >> 1) & 7);
 }
-__device__ inline int v_swizzle(int d) { return (d & 15) ^ ((d >> 3) & 15); }
 
 template <int D, int NTW>
 struct Geo {
   static constexpr int CPK = D / 8;          // 16-byte chunks per K/V row of one head
   static constexpr int KPL = 64 / CPK;       // keys covered by one wave-wide 16-byte load
-  static constexpr int NLOAD = 32 / KPL;     // such loads per lane, per tensor, per stage
+  static constexpr int NW = kAttnWaves;     // waves per workgroup
+  static constexpr int KPW = kStageKeys / NW;  // keys each wave fetches per stage
+  static constexpr int NL = KPW / KPL;       // wave-wide loads per wave, per tensor, per stage
   static constexpr int DC = D / 32;          // 32-channel steps of the QK contraction
   static constexpr int DT = D / 16;          // 16-channel output tiles
   static constexpr int WROWS = 16 * NTW;     // rows one wave owns
-  static constexpr int RT = 4 * WROWS;       // rows per tile
-  static constexpr int KBYTES = kStageKeys * D * 2;
-  static constexpr int LDS = 2 * KBYTES;     // K tile + V^T tile
+  static constexpr int RT = NW * WROWS;      // rows per tile
+  static constexpr int ROWB = 2 * D;         // bytes of one key row in LDS
+  static constexpr int TILEB = kStageKeys * ROWB;
+  static constexpr int STAGEB = 2 * TILEB;   // K tile + V tile
+  static constexpr int NBUF = 4;
+  static constexpr int LDS = NBUF * STAGEB;
   static constexpr int MERGE_SLOT = DT * 256 + 32;  // floats per (wave, n-tile) in the merge buffer
-  static_assert(3 * NTW * MERGE_SLOT * 4 <= LDS, "merge buffer must fit the stage buffer");
+  static_assert((NW - 1) * NTW * MERGE_SLOT * 4 <= LDS, "merge buffer must fit the ring");
+  static_assert(NL >= 1 && KPW % KPL == 0, "stage split");
 };
 
 template <int D, int NTW>
-__global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParams p) {
   using T = Geo<D, NTW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
   __shared__ int s_item;
-  unsigned char* const Ks = smem;
-  unsigned char* const Vt = smem + T::KBYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,6 +123,15 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p)
   const __bf16* const qg = static_cast<const __bf16*>(p.q);
   __bf16* const og = static_cast<__bf16*>(p.out);
   const float sl2 = p.scale_log2;
+  // LDS byte address of the ring (DMA destinations are given as LDS addresses).
+  const unsigned lds_ring = static_cast<unsigned>(reinterpret_cast<size_t>((LDS_AS unsigned char*)smem));
+
+  // Lane-constant parts of the fragment addresses.
+  // V^T operand via ds_read_b64_tr_b16: in each 16-lane group the 16 lanes point at 4 keys x 4 groups of
+  // 4 channels; lane i of group g4 points at key 4*g4 + i/4, channels 4*(i%4) .. +3 of the 16-channel tile.
+  const int tr_key = 4 * g4 + (l16 >> 2);
+  const int tr_half = (l16 & 1) << 3;       // byte offset inside the 16-byte chunk
+  const int tr_chunk = (l16 & 3) >> 1;      // chunk offset inside the 16-channel tile
 
   for (;;) {
     if (tid == 0) s_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
@@ -110,12 +152,50 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p)
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;
     const int kb = part * P;
     const int ke = min(kmax, kb + P);
-    const int WR = rows_here <= T::WROWS ? 1 : (rows_here <= 2 * T::WROWS ? 2 : 4);
-    const int WK = 4 / WR;
+    const int WR = rows_here <= T::WROWS ? 1
+                   : rows_here <= 2 * T::WROWS ? 2
+                   : rows_here <= 4 * T::WROWS ? 4 : 8;
+    const int WK = T::NW / WR;
     const int wr = wave / WK;
     const int wk = wave - wr * WK;
     const int my_row0 = row0 + wr * T::WROWS;
-    const int* const tbl = p.block_tables + static_cast<int64_t>(s) * p.max_blocks_per_seq;
+    const CONST_AS int* const tbl =
+        (const CONST_AS int*)(p.block_tables + static_cast<int64_t>(s) * p.max_blocks_per_seq);
+    const int nst = (ke - kb + kStageKeys - 1) / kStageKeys;
+
+    // Physical blocks of this wave's NL loads of stage st (scalar loads; keys past ke clamp to ke-1).
+    auto fetch_table = [&](int st, int* phys) {
+#pragma unroll
+      for (int i = 0; i < T::NL; ++i) {
+        const int kfirst = min(kb + st * kStageKeys + T::KPW * wave + T::KPL * i, ke - 1);
+        phys[i] = tbl[kfirst >> bs_log2];
+      }
+    };
+    // Wave w fetches keys [KPW*w, KPW*(w+1)) of stage st into ring slot st % NBUF.  Keys at or past ke are
+    // clamped to row ke-1 of the same block (a wave-wide load never spans two blocks); their scores are
+    // masked, so those rows carry probability 0, and rows past the context are never read.
+    auto issue = [&](int st, const int* phys) {
+      unsigned char* const kdst = smem + (st & (T::NBUF - 1)) * T::STAGEB;
+      const int key0 = kb + st * kStageKeys + T::KPW * wave;
+#pragma unroll
+      for (int i = 0; i < T::NL; ++i) {
+        const int key_local = T::KPW * wave + T::KPL * i + lane / T::CPK;
+        const int kk = min(key0 + T::KPL * i + lane / T::CPK, ke - 1);
+        const int ph = min(max(phys[i], 0), last_block);
+        const int c = (lane % T::CPK) ^ k_swizzle<D>(key_local);
+        const int64_t e = static_cast<int64_t>(ph) * p.block_stride +
+                          (static_cast<int64_t>(kk & bs_mask) * Hkv + g) * D + c * 8;
+        const unsigned dk = lds_ring + static_cast<unsigned>((kdst - smem) + (T::KPW * wave + T::KPL * i) * T::ROWB);
+        dma16(kc + e, dk);
+        dma16(vc + e, dk + T::TILEB);
+      }
+    };
+
+    int tb0[T::NL], tb1[T::NL], tb2[T::NL], tbn[T::NL];
+    fetch_table(0, tb0);
+    if (nst > 1) fetch_table(1, tb1);
+    if (nst > 2) fetch_table(2, tb2);
+    if (nst > 3) fetch_table(3, tbn);
 
     // Query fragments: B operand of S^T = K Q^T.  Lane holds row l16, channels 32*dc + 8*g4 + [0, 8).
     bf16x8 qf[NTW][T::DC];
@@ -137,6 +217,13 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p)
       }
     }
 
+    // The query fragments must be in registers before the stage copies are issued: the compiler does not
+    // count the copies, so any wait it placed for q inside the loop would drain them every stage.
+    wait_vmem<0>();
+    issue(0, tb0);
+    if (nst > 1) issue(1, tb1);
+    if (nst > 2) issue(2, tb2);
+
     f32x4 acc[NTW][T::DT];
     float m[NTW], lsum[NTW];
 #pragma unroll
@@ -147,123 +234,83 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p)
       for (int dt = 0; dt < T::DT; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int nst = (ke - kb + kStageKeys - 1) / kStageKeys;
-    u32x4 kreg[T::NLOAD], vreg[T::NLOAD];
-
-    // Block-table entries for one stage: lane i (< NLOAD) fetches the physical block of this wave's
-    // i-th wave-wide load.  Fetched a stage ahead so the data loads never wait on a table lookup.
-    auto fetch_table = [&](int st) -> int {
-      const int i = lane < T::NLOAD ? lane : T::NLOAD - 1;
-      const int kk0 = min(kb + st * kStageKeys + 32 * wave + T::KPL * i, ke - 1);
-      return tbl[kk0 >> bs_log2];
-    };
-    // Wave w loads keys [32w, 32w+32) of stage st.  Keys at or past ke are clamped to row ke-1 of the
-    // same block (a wave-wide load never spans two blocks); their scores are masked, so the duplicate
-    // rows carry probability 0 and rows past the context are never read.
-    auto issue = [&](int st, int tv) {
-      const int kbase = kb + st * kStageKeys + 32 * wave;
-#pragma unroll
-      for (int i = 0; i < T::NLOAD; ++i) {
-        const int phys = min(max(__builtin_amdgcn_readlane(tv, i), 0), last_block);
-        const int kk = min(kbase + T::KPL * i + lane / T::CPK, ke - 1);
-        const int64_t e = static_cast<int64_t>(phys) * p.block_stride +
-                          (static_cast<int64_t>(kk & bs_mask) * Hkv + g) * D + (lane % T::CPK) * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(kc + e);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vc + e);
-      }
-    };
-
-    int tv = fetch_table(0);
-    issue(0, tv);
-    if (nst > 1) tv = fetch_table(1);
     for (int st = 0; st < nst; ++st) {
-      __syncthreads();  // every wave is done reading the previous stage
-#pragma unroll
-      for (int i = 0; i < T::NLOAD; ++i) {
-        const int key = 32 * wave + T::KPL * i + lane / T::CPK;
-        const int c = lane % T::CPK;
-        *reinterpret_cast<u32x4*>(Ks + key * (D * 2) + ((c ^ k_swizzle<D>(key)) << 4)) = kreg[i];
-        // V^T: key kk of the 32-key step goes to position 8*((kk&15)>>2) + (kk&3) + 4*(kk>>4), which is
-        // where the S^T fragments of the two 16-key halves put its probability.
-        const int kk = key & 31;
-        const int chunk = (wave << 2) + ((kk & 15) >> 2);
-        const int jj = (kk & 3) + ((kk >> 4) << 2);
-        const bf16x8 vb = as_bf16x8(vreg[i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * c + e;
-          *reinterpret_cast<__bf16*>(Vt + d * 256 + ((chunk ^ v_swizzle(d)) << 4) + jj * 2) = vb[e];
-        }
-      }
-      __syncthreads();
-      if (st + 1 < nst) {
-        issue(st + 1, tv);
-        if (st + 2 < nst) tv = fetch_table(st + 2);
-      }
+      // Stage st has landed once at most the later stages' loads are outstanding.
+      const int later = min(2, nst - 1 - st);
+      if (later == 2) wait_vmem<4 * T::NL>();
+      else if (later == 1) wait_vmem<2 * T::NL>();
+      else wait_vmem<0>();
+      __syncthreads();  // all waves' loads of stage st landed; all waves done with stage st-1
+      if (st + 3 < nst) issue(st + 3, tbn);
 
+      const unsigned char* const Ks = smem + (st & (T::NBUF - 1)) * T::STAGEB;
+      const unsigned char* const Vs = Ks + T::TILEB;
       const int kstage = kb + st * kStageKeys;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if ((c % WK) != wk || kstage + 32 * c >= ke) continue;
-        // S^T for keys 32c + [0, 32): two 16-key M tiles.
-        f32x4 sacc[NTW][2];
+      for (int j = 0; j < 4; ++j) {
+        if (((st * 4 + j) % WK) != wk || kstage + 16 * j >= ke) continue;
+        // S^T for keys 16j + [0, 16).
+        f32x4 sacc[NTW];
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) sacc[nt][0] = sacc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int key = 32 * c + 16 * mt + l16;
+        for (int nt = 0; nt < NTW; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+          const int key = 16 * j + l16;
 #pragma unroll
           for (int dc = 0; dc < T::DC; ++dc) {
             const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                Ks + key * (D * 2) + (((4 * dc + g4) ^ k_swizzle<D>(key)) << 4)));
+                Ks + key * T::ROWB + (((4 * dc + g4) ^ k_swizzle<D>(key)) << 4)));
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) sacc[nt][mt] = mfma16x16x32(kf, qf[nt][dc], sacc[nt][mt]);
+            for (int nt = 0; nt < NTW; ++nt) sacc[nt] = mfma_qk(kf, qf[nt][dc], sacc[nt]);
           }
         }
-        // Online softmax; lane holds keys kabs0 + 16*mt + j of row l16.
-        const int kabs0 = kstage + 32 * c + 4 * g4;
-        bf16x8 pf[NTW];
+        // Online softmax; the lane holds keys kabs0 + [0, 4) of row l16.
+        const int kabs0 = kstage + 16 * j + 4 * g4;
+        i16x4 pf[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-          float sv[8];
+          float sv[4];
           float cm = -INFINITY;
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float x = sacc[nt][mt][j] * sl2;
-              const float y = (kabs0 + 16 * mt + j <= lim[nt]) ? x : -INFINITY;
-              sv[mt * 4 + j] = y;
-              cm = fmaxf(cm, y);
-            }
+          for (int jj = 0; jj < 4; ++jj) {
+            const float x = sacc[nt][jj] * sl2;
+            sv[jj] = (kabs0 + jj <= lim[nt]) ? x : -INFINITY;
+            cm = fmaxf(cm, sv[jj]);
           }
           cm = fmaxf(cm, __shfl_xor(cm, 16));
           cm = fmaxf(cm, __shfl_xor(cm, 32));
           const float mnew = fmaxf(m[nt], cm);
           const float mref = mnew == -INFINITY ? 0.f : mnew;
           const float alpha = __builtin_amdgcn_exp2f(m[nt] - mref);
+          bf16x4 pb;
           float ps = 0.f;
 #pragma unroll
-          for (int k8 = 0; k8 < 8; ++k8) {
-            const float pv = __builtin_amdgcn_exp2f(sv[k8] - mref);
+          for (int jj = 0; jj < 4; ++jj) {
+            const float pv = __builtin_amdgcn_exp2f(sv[jj] - mref);
             ps += pv;
-            pf[nt][k8] = static_cast<__bf16>(pv);
+            pb[jj] = static_cast<__bf16>(pv);
           }
+          pf[nt] = __builtin_bit_cast(i16x4, pb);
           lsum[nt] = lsum[nt] * alpha + ps;
           m[nt] = mnew;
 #pragma unroll
           for (int dt = 0; dt < T::DT; ++dt) acc[nt][dt] *= alpha;
         }
-        // O^T += V^T P^T over the 32 keys.
+        // O^T += V^T P^T over the 16 keys.
+        {
+          const int key = 16 * j + tr_key;
+          const unsigned char* const vrow = Vs + key * T::ROWB + tr_half;
+          const int sw = k_swizzle<D>(key);
 #pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const int d = 16 * dt + l16;
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              Vt + d * 256 + ((((c << 2) + g4) ^ v_swizzle(d)) << 4)));
+          for (int dt = 0; dt < T::DT; ++dt) {
+            const int chunk = (2 * dt + tr_chunk) ^ sw;
+            const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS i16x4*)(vrow + (chunk << 4)));
 #pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) acc[nt][dt] = mfma16x16x32(vf, pf[nt], acc[nt][dt]);
+            for (int nt = 0; nt < NTW; ++nt) acc[nt][dt] = mfma_pv(vf, pf[nt], acc[nt][dt]);
+          }
         }
       }
+      if (st + 4 < nst) fetch_table(st + 4, tbn);
     }
 
 #pragma unroll
@@ -346,15 +393,15 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(const AttnParams p)
 
 int attention_bf16_wgs_per_cu(int head_dim, int tile_kind) {
   (void)tile_kind;
-  // 160 KiB of LDS per CU; the stage buffer is 2 * 128 keys * head_dim * 2 bytes.
-  const int lds = 2 * kStageKeys * head_dim * 2 + 64;
+  // 160 KiB of LDS per CU; the ring is 4 stages x 64 keys x (K + V) x head_dim x 2 bytes.
+  const int lds = 4 * 2 * kStageKeys * head_dim * 2 + 64;
   int wgs = (160 * 1024) / lds;
-  return wgs > 4 ? 4 : wgs;
+  return wgs < 1 ? 1 : (wgs > 2 ? 2 : wgs);
 }
 
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
                                  hipStream_t stream) {
-  const dim3 g(static_cast<unsigned>(grid)), b(kThreads);
+  const dim3 g(static_cast<unsigned>(grid)), b(kAttnThreads);
   if (head_dim == 128) {
     if (tile_kind == 2) hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), g, b, 0, stream, p);
     else hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);

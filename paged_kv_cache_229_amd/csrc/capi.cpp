@@ -89,7 +89,7 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
                           int32_t head_dim, int tile_kind) {
   WsLayout w{};
   const int group = num_q_heads / num_kv_heads;
-  w.rows_per_tile = tile_kind == 2 ? 128 : 64;
+  w.rows_per_tile = pkv::kAttnWaves * 16 * (tile_kind == 2 ? 2 : 1);
   // Each sequence adds at most one partly filled tile.
   w.tile_cap = (total_q * group + w.rows_per_tile - 1) / w.rows_per_tile + num_seqs;
   w.unit_cap = (pkv::kMaxItems + num_kv_heads - 1) / num_kv_heads + w.tile_cap;

@@ -6,9 +6,13 @@
 
 namespace pkv {
 
-// Keys staged in LDS per step of the attention main loop: 4 waves x 32 keys.
-constexpr int kStageKeys = 128;
+// Keys staged in LDS per stage of the attention main loop: 8 waves x 8 keys.  Partitions are multiples
+// of it.
+constexpr int kStageKeys = 64;
 constexpr int kThreads = 256;
+// The bf16 attention workgroup: 8 waves (two per SIMD).
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
 constexpr int kDefaultItems = 1024;
@@ -84,7 +88,8 @@ struct KvWriteParams {
 
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
-// tile_kind 1: 64-row tiles, 2: 128-row tiles.  grid = persistent workgroups.
+// tile_kind 1: 16 rows per wave (128-row tiles), 2: 32 rows per wave (256-row tiles).
+// grid = persistent workgroups.
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
                                  hipStream_t stream);
 hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream);
