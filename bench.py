@@ -182,10 +182,10 @@ def main() -> None:
     sm, cl, qsl = t(st.slot_mapping, False), t(st.context_lens, False), t(st.query_start_loc, False)
     max_q = int(np.diff(st.query_start_loc).max())
     out = torch.empty_like(q)
+    pkv.set_tuning(args.partition, args.items, args.tile_kind)  # the workspace size depends on it
     ws = torch.empty(max(256, pkv.workspace_size(w.num_seqs, q.shape[0], w.num_q_heads,
                                                  w.num_kv_heads, w.head_dim, q.dtype, max_q)),
                      dtype=torch.uint8, device=dev)
-    pkv.set_tuning(args.partition, args.items, args.tile_kind)
 
     def step(i):
         kp, vp = copies[i % len(copies)]

@@ -21,10 +21,11 @@
 //    keeps the fragment reads conflict-free.  The swizzle is applied on the way in by choosing which lane
 //    loads which chunk (the DMA writes lane l's 16 bytes at offset 16*l).
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16 (16 keys as M, 16 rows
-//    as N): each lane owns one row (lane % 16) for the 4 keys it holds, so row max and row sum need two
-//    cross-lane exchanges, and the probabilities already sit in the B-operand layout of
-//    O^T += V^T P^T (v_mfma_f32_16x16x16_bf16, 16 keys as K).  The V^T operand (4 keys of one channel per
-//    lane) is read from the row-major V tile with ds_read_b64_tr_b16, one read per MFMA.
+//    as N): each lane owns one row (lane % 16) for the 8 keys it holds of a 32-key chunk, so row max and
+//    row sum need two cross-lane exchanges per chunk, and the probabilities already sit in the B-operand
+//    layout of O^T += V^T P^T (v_mfma_f32_16x16x32_bf16, 32 keys as K, taken in the order the S^T
+//    fragments deliver them).  The matching V^T operand (8 keys of one channel per lane) is read from the
+//    row-major V tile with two ds_read_b64_tr_b16.
 //  * Online softmax in log2 units (scale * log2 e folded into the score scale), exp2 on the VALU.
 //  * Waves split a tile's rows when it has many (prefill, speculative decode), or the keys when it has
 //    few (decode); in the latter case the waves' softmax states are merged through LDS at the end.
@@ -47,11 +48,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// D[m][n] += sum_k A[m][k] B[k][n] over a 16x16x32 tile; lane l holds A[l%16][8(l/16) + 0..7],
+// B[8(l/16) + 0..7][l%16] and D[4(l/16) + 0..3][l%16].
 __device__ inline f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ inline f32x4 mfma_pv(i16x4 a, i16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // 16-byte HBM -> LDS copy per lane: lane l's 16 bytes from `src` land at LDS byte address
@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
     const int unit = item / Hkv;
     const int g = item - unit * Hkv;
     const int4 u = p.buf.units[unit];
-    const int s = u.x, tile = u.y, part = u.z, nparts = u.w;
+    const int s = u.x, tile = u.y, part = u.z, pbase = u.w;
     const int q0 = p.query_start_loc[s];
     const int n = p.query_start_loc[s + 1] - q0;
     const int L = p.context_lens[s];
@@ -248,67 +248,78 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
       const unsigned char* const Ks = smem + (st & (T::NBUF - 1)) * T::STAGEB;
       const unsigned char* const Vs = Ks + T::TILEB;
       const int kstage = kb + st * kStageKeys;
+      // Two 32-key chunks per stage; chunk number st*2+c goes to the key-group (st*2+c) % WK.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (((st * 4 + j) % WK) != wk || kstage + 16 * j >= ke) continue;
-        // S^T for keys 16j + [0, 16).
-        f32x4 sacc[NTW];
+      for (int c = 0; c < 2; ++c) {
+        if (((st * 2 + c) % WK) != wk || kstage + 32 * c >= ke) continue;
+        // S^T for keys 32c + 16mt + [0, 16), mt = 0, 1.
+        f32x4 sacc[NTW][2];
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        {
-          const int key = 16 * j + l16;
+        for (int nt = 0; nt < NTW; ++nt) sacc[nt][0] = sacc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int key = 32 * c + 16 * mt + l16;
 #pragma unroll
           for (int dc = 0; dc < T::DC; ++dc) {
             const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
                 Ks + key * T::ROWB + (((4 * dc + g4) ^ k_swizzle<D>(key)) << 4)));
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) sacc[nt] = mfma_qk(kf, qf[nt][dc], sacc[nt]);
+            for (int nt = 0; nt < NTW; ++nt) sacc[nt][mt] = mfma_qk(kf, qf[nt][dc], sacc[nt][mt]);
           }
         }
-        // Online softmax; the lane holds keys kabs0 + [0, 4) of row l16.
-        const int kabs0 = kstage + 16 * j + 4 * g4;
-        i16x4 pf[NTW];
+        // Online softmax over the 32 keys; the lane holds keys kabs0 + 16*mt + [0, 4) of row l16.
+        const int kabs0 = kstage + 32 * c + 4 * g4;
+        bf16x8 pf[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-          float sv[4];
+          float sv[8];
           float cm = -INFINITY;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float x = sacc[nt][jj] * sl2;
-            sv[jj] = (kabs0 + jj <= lim[nt]) ? x : -INFINITY;
-            cm = fmaxf(cm, sv[jj]);
+          for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const float x = sacc[nt][mt][jj] * sl2;
+              const float y = (kabs0 + 16 * mt + jj <= lim[nt]) ? x : -INFINITY;
+              sv[4 * mt + jj] = y;
+              cm = fmaxf(cm, y);
+            }
           }
           cm = fmaxf(cm, __shfl_xor(cm, 16));
           cm = fmaxf(cm, __shfl_xor(cm, 32));
           const float mnew = fmaxf(m[nt], cm);
           const float mref = mnew == -INFINITY ? 0.f : mnew;
           const float alpha = __builtin_amdgcn_exp2f(m[nt] - mref);
-          bf16x4 pb;
           float ps = 0.f;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float pv = __builtin_amdgcn_exp2f(sv[jj] - mref);
+          for (int k8 = 0; k8 < 8; ++k8) {
+            const float pv = __builtin_amdgcn_exp2f(sv[k8] - mref);
             ps += pv;
-            pb[jj] = static_cast<__bf16>(pv);
+            pf[nt][k8] = static_cast<__bf16>(pv);
           }
-          pf[nt] = __builtin_bit_cast(i16x4, pb);
           lsum[nt] = lsum[nt] * alpha + ps;
           m[nt] = mnew;
 #pragma unroll
           for (int dt = 0; dt < T::DT; ++dt) acc[nt][dt] *= alpha;
         }
-        // O^T += V^T P^T over the 16 keys.
+        // O^T += V^T P^T over the 32 keys (v_mfma_f32_16x16x32_bf16): the contraction index 8*g4 + t is key
+        // 4*g4 + t of the first 16-key half for t < 4 and of the second half for t >= 4, which is where the
+        // S^T fragments put the probabilities; one transpose read per half gives the matching V^T operand.
         {
-          const int key = 16 * j + tr_key;
-          const unsigned char* const vrow = Vs + key * T::ROWB + tr_half;
-          const int sw = k_swizzle<D>(key);
+          const int key_a = 32 * c + tr_key;
+          const int key_b = key_a + 16;
+          const unsigned char* const va = Vs + key_a * T::ROWB + tr_half;
+          const unsigned char* const vb = Vs + key_b * T::ROWB + tr_half;
+          const int swa = k_swizzle<D>(key_a);
+          const int swb = k_swizzle<D>(key_b);
 #pragma unroll
           for (int dt = 0; dt < T::DT; ++dt) {
-            const int chunk = (2 * dt + tr_chunk) ^ sw;
-            const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_AS i16x4*)(vrow + (chunk << 4)));
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS i16x4*)(va + (((2 * dt + tr_chunk) ^ swa) << 4)));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS i16x4*)(vb + (((2 * dt + tr_chunk) ^ swb) << 4)));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) acc[nt][dt] = mfma_pv(vf, pf[nt], acc[nt][dt]);
+            for (int nt = 0; nt < NTW; ++nt) acc[nt][dt] = mfma_qk(vf, pf[nt], acc[nt][dt]);
           }
         }
       }
@@ -365,7 +376,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
       for (int nt = 0; nt < NTW; ++nt) {
         const int r = my_row0 + nt * 16 + l16;
         if (r >= row0 + rows_here) continue;
-        if (nparts == 1) {
+        if (pbase < 0) {
           const int i = r / G;
           const int hh = r - i * G;
           const float inv = 1.f / lsum[nt];
@@ -380,7 +391,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
             *reinterpret_cast<bf16x4*>(o + 16 * dt) = v;
           }
         } else {
-          const int64_t prow = static_cast<int64_t>(item) * T::RT + (r - row0);
+          const int64_t prow = static_cast<int64_t>(pbase) + g * rows_here + (r - row0);
           float* const pa = p.buf.part_acc + prow * D + 4 * g4;
 #pragma unroll
           for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(pa + 16 * dt) = acc[nt][dt];

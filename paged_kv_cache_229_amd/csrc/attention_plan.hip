@@ -9,7 +9,8 @@
 // so a tile holds several tokens' worth of grouped heads and the keys it loads serve all of them.  Row
 // tile t covers rows [t*RT, min(rows, (t+1)*RT)); its last token sees keys [0, kmax).  A tile whose kmax
 // exceeds the partition length P is split into ceil(kmax / P) partitions; P is picked so the whole call
-// has about `target_items` (unit, kv head) items, enough to fill 256 compute units several times over.
+// has about `target_items` (unit, kv head) items, enough to fill 256 compute units several times over,
+// and then lengthened until the split tiles' partial rows fit the workspace.
 // Each partition of a split tile leaves (acc, m, l) per row; split_reduce_kernel merges them:
 //     M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // (m in log2 units: the main kernel folds log2(e) into the score scale).
@@ -121,22 +122,28 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
     if (P < kMinPartition) P = kMinPartition;
   }
 
-  long long units_total = 0, unit_off = 0;
+  // Partitions per tile and partial rows per split tile, for partition length P.
+  long long units_total = 0, unit_off = 0, prows_total = 0, prow_off = 0;
   for (;;) {
-    long long units = 0;
+    long long units = 0, prows = 0;
     for (int s = s0; s < s1; ++s) {
       const int nt = p.buf.seq_tiles[s];
       if (nt == 0) continue;
       const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
       const int rows = n * G;
-      for (int tt = 0; tt < nt; ++tt) units += (tile_kmax(L, n, G, rows, RT, tt) + P - 1) / P;
+      for (int tt = 0; tt < nt; ++tt) {
+        const long long np = (tile_kmax(L, n, G, rows, RT, tt) + P - 1) / P;
+        units += np;
+        if (np > 1) prows += np * min(RT, rows - tt * RT) * p.num_kv_heads;
+      }
     }
     unit_off = block_exclusive_scan(units, &units_total, sm);
-    if (units_total <= p.unit_cap || P >= max_kmax) break;
+    prow_off = block_exclusive_scan(prows, &prows_total, sm);
+    if ((units_total <= p.unit_cap && prows_total <= p.prow_cap) || P >= max_kmax) break;
     P *= 2;
   }
 
-  long long tb = tile_off, ub = unit_off;
+  long long tb = tile_off, ub = unit_off, pr = prow_off;
   for (int s = s0; s < s1; ++s) {
     p.buf.tile_base[s] = static_cast<int>(tb);
     const int nt = p.buf.seq_tiles[s];
@@ -145,9 +152,17 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
     const int rows = n * G;
     for (int tt = 0; tt < nt; ++tt) {
       const int np = static_cast<int>((tile_kmax(L, n, G, rows, RT, tt) + P - 1) / P);
+      const int rows_t = min(RT, rows - tt * RT);
       p.buf.tile_rec[tb] = make_int2(static_cast<int>(ub), np);
       ++tb;
-      for (int pp = 0; pp < np; ++pp) p.buf.units[ub++] = make_int4(s, tt, pp, np);
+      for (int pp = 0; pp < np; ++pp) {
+        int pb = -1;
+        if (np > 1) {
+          pb = static_cast<int>(pr);
+          pr += static_cast<long long>(rows_t) * p.num_kv_heads;
+        }
+        p.buf.units[ub++] = make_int4(s, tt, pp, pb);
+      }
     }
   }
   if (t == 0) {
@@ -181,19 +196,20 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
   for (int w = threadIdx.x; w < rows_here * D4; w += kThreads) {
     const int rl = w / D4;
     const int d0 = (w - rl * D4) * 4;
+    const int row_off = g * rows_here + rl;
     float M = -INFINITY;
     for (int pp = 0; pp < rec.y; ++pp) {
-      const int64_t item = static_cast<int64_t>(rec.x + pp) * p.num_kv_heads + g;
-      M = fmaxf(M, p.buf.part_ml[item * RT + rl].x);
+      const int64_t prow = p.buf.units[rec.x + pp].w + row_off;
+      M = fmaxf(M, p.buf.part_ml[prow].x);
     }
     const float mref = M == -INFINITY ? 0.f : M;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, den = 0.f;
     for (int pp = 0; pp < rec.y; ++pp) {
-      const int64_t item = static_cast<int64_t>(rec.x + pp) * p.num_kv_heads + g;
-      const float2 ml = p.buf.part_ml[item * RT + rl];
+      const int64_t prow = p.buf.units[rec.x + pp].w + row_off;
+      const float2 ml = p.buf.part_ml[prow];
       const float wgt = __builtin_amdgcn_exp2f(ml.x - mref);
       den += wgt * ml.y;
-      const float4 a = *reinterpret_cast<const float4*>(p.buf.part_acc + (item * RT + rl) * D + d0);
+      const float4 a = *reinterpret_cast<const float4*>(p.buf.part_acc + prow * D + d0);
       a0 += wgt * a.x;
       a1 += wgt * a.y;
       a2 += wgt * a.z;

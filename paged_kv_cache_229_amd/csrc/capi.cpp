@@ -106,7 +106,7 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   off = round256(off + static_cast<size_t>(w.tile_cap) * 2 * sizeof(int));
   w.units = off;
   off = round256(off + static_cast<size_t>(w.unit_cap) * 4 * sizeof(int));
-  const size_t part_rows = static_cast<size_t>(w.unit_cap) * num_kv_heads * w.rows_per_tile;
+  const size_t part_rows = pkv::kPartialRowCap;
   w.part_ml = off;
   off = round256(off + part_rows * 2 * sizeof(float));
   w.part_acc = off;
@@ -283,6 +283,7 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
   pp.forced_partition = g_partition_keys;
   pp.unit_cap = static_cast<int>(w.unit_cap);
   pp.tile_cap = static_cast<int>(w.tile_cap);
+  pp.prow_cap = pkv::kPartialRowCap;
   pp.buf = b;
 
   hipError_t e = pkv::launch_plan(pp, st);

@@ -29,10 +29,14 @@ struct PlanBuffers {
   int* seq_units;   // [num_seqs]  scratch
   int* tile_base;   // [num_seqs + 1] first tile record of each sequence
   int2* tile_rec;   // [tile_cap]  {first unit, number of partitions}
-  int4* units;      // [unit_cap]  {sequence, tile, partition, partitions of the tile}
-  float2* part_ml;  // [unit_cap * H_kv * rows_per_tile]  running max (log2 units) and sum per row
-  float* part_acc;  // [unit_cap * H_kv * rows_per_tile * head_dim] unnormalised partial outputs
+  int4* units;      // [unit_cap]  {sequence, tile, partition, first partial row or -1 if unsplit}
+  float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
+  float* part_acc;  // [prow_cap * head_dim] unnormalised partial outputs
 };
+
+// Partial rows of a split unit u (tile with `rows` rows): [u.w, u.w + H_kv * rows), kv head g's rows at
+// u.w + g * rows.
+constexpr int kPartialRowCap = 1 << 17;
 
 struct PlanParams {
   const int* context_lens;
@@ -47,6 +51,7 @@ struct PlanParams {
   int forced_partition;
   int unit_cap;
   int tile_cap;
+  int prow_cap;
   PlanBuffers buf;
 };
 
