@@ -57,6 +57,26 @@ def algorithmic_work(w) -> dict:
                 prefill_flops=4 * d * hq * pairs_pre)
 
 
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy
+    calibration) as recorded in profiles/attn_traffic.json, or None when the kernel source has changed
+    since those counters were taken (or none were taken for this workload)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec.get("sources", []):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else int(w["read_bytes"] + w["write_bytes"])
+
+
 class HipEvents:
     """hipEvent_t pairs from the HIP runtime torch already loaded (same soname)."""
 
@@ -241,7 +261,7 @@ def main() -> None:
         "attention_tflops": round(work["flops"] / (k_avg * 1e-3) / 1e12, 2),
         "attention_logical_gbs": round(work["attn_bytes_logical"] / (k_avg * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
                      "kernel": "attn_bf16_kernel",
                      "bytes_per_launch": work["attn_bytes_unique"]},
     }
