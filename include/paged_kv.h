@@ -134,8 +134,7 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
  *                   multiple of 128); 0 = chosen per call from the lengths on the device.
  *   target_items    > 0: aim the automatic choice at this many (tile, kv head, partition) work items;
  *                   0 = default.
- *   tile_kind       0 = automatic; 1 = 16 rows per wave (128-row tiles); 2 = 32 rows per wave
- *                   (256-row tiles) (bf16 path).
+ *   tile_kind       0 = automatic; 1 = 128-row tiles (the only tile shape of this version).
  */
 int paged_attention_set_tuning(int32_t partition_keys, int32_t target_items, int32_t tile_kind);
 

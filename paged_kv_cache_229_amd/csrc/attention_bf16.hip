@@ -91,6 +91,7 @@ struct Geo {
   static constexpr int DT = D / 16;          // 16-channel output tiles
   static constexpr int WROWS = 16 * NTW;     // rows one wave owns
   static constexpr int RT = NW * WROWS;      // rows per tile
+  static_assert(RT == kTileRows, "the plan and the kernel agree on the tile height");
   static constexpr int ROWB = 2 * D;         // bytes of one key row in LDS
   static constexpr int TILEB = kStageKeys * ROWB;
   static constexpr int STAGEB = 2 * TILEB;   // K tile + V tile
@@ -414,14 +415,10 @@ int attention_bf16_wgs_per_cu(int head_dim, int tile_kind) {
 
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
                                  hipStream_t stream) {
+  (void)tile_kind;
   const dim3 g(static_cast<unsigned>(grid)), b(kAttnThreads);
-  if (head_dim == 128) {
-    if (tile_kind == 2) hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);
-  } else {
-    if (tile_kind == 2) hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), g, b, 0, stream, p);
-  }
+  if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);
+  else hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), g, b, 0, stream, p);
   return hipGetLastError();
 }
 

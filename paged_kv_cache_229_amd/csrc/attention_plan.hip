@@ -10,7 +10,10 @@
 // tile t covers rows [t*RT, min(rows, (t+1)*RT)); its last token sees keys [0, kmax).  A tile whose kmax
 // exceeds the partition length P is split into ceil(kmax / P) partitions; P is picked so the whole call
 // has about `target_items` (unit, kv head) items, enough to fill 256 compute units several times over,
-// and then lengthened until the split tiles' partial rows fit the workspace.
+// and then lengthened until the split tiles' partial rows fit the workspace.  Units are listed longest
+// first (counting sort on their 64-key stage count) so that the attention kernel's static, snake-ordered
+// assignment of items to workgroups stays balanced.
+//
 // Each partition of a split tile leaves (acc, m, l) per row; split_reduce_kernel merges them:
 //     M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // (m in log2 units: the main kernel folds log2(e) into the score scale).
@@ -23,6 +26,8 @@ namespace pkv {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kSortBuckets = 1024;
 
 __device__ inline bool seq_ok(int q_lo, int q_hi, int context_len, int64_t total_q, int max_context) {
   return q_lo >= 0 && q_hi >= q_lo && q_hi <= total_q && context_len >= q_hi - q_lo &&
@@ -35,38 +40,57 @@ __device__ inline int tile_kmax(int context_len, int n, int group, int rows, int
   return context_len - n + last_row / group + 1;
 }
 
-// Exclusive prefix sum over the workgroup; *total receives the sum of all values.
+// Stage-count bucket of a unit, longest first.
+__device__ inline int sort_bucket(int keys) {
+  const int stages = (keys + kStageKeys - 1) / kStageKeys;
+  return kSortBuckets - 1 - min(stages, kSortBuckets - 1);
+}
+
+// Exclusive prefix sum over the workgroup (wave scans, then a scan of the wave totals);
+// *total receives the sum of all values.  `sm` holds kPlanWaves + 1 entries.
 __device__ long long block_exclusive_scan(long long v, long long* total, long long* sm) {
   const int t = threadIdx.x;
-  sm[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const long long x = t >= off ? sm[t - off] : 0;
-    __syncthreads();
-    sm[t] += x;
-    __syncthreads();
+  const int lane = t & 63, wave = t >> 6;
+  long long incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long x = __shfl_up(incl, off);
+    if (lane >= off) incl += x;
   }
-  const long long incl = sm[t];
-  *total = sm[kPlanThreads - 1];
+  if (lane == 63) sm[wave] = incl;
   __syncthreads();
-  return incl - v;
+  if (t == 0) {
+    long long run = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const long long x = sm[w];
+      sm[w] = run;
+      run += x;
+    }
+    sm[kPlanWaves] = run;
+  }
+  __syncthreads();
+  const long long excl = sm[wave] + incl - v;
+  *total = sm[kPlanWaves];
+  __syncthreads();
+  return excl;
 }
 
 __device__ long long block_max(long long v, long long* sm) {
   const int t = threadIdx.x;
-  sm[t] = v;
+  const int lane = t & 63, wave = t >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<long long>(__shfl_xor(v, off)));
+  if (lane == 0) sm[wave] = v;
   __syncthreads();
-  for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
-    if (t < off) sm[t] = max(sm[t], sm[t + off]);
-    __syncthreads();
-  }
-  const long long r = sm[0];
+  long long r = sm[0];
+  for (int w = 1; w < kPlanWaves; ++w) r = max(r, sm[w]);
   __syncthreads();
   return r;
 }
 
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) {
-  __shared__ long long sm[kPlanThreads];
+  __shared__ long long sm[kPlanWaves + 1];
+  __shared__ int bucket[kSortBuckets];
   const int t = threadIdx.x;
   const int N = p.num_seqs;
   const int per = (N + kPlanThreads - 1) / kPlanThreads;
@@ -123,7 +147,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
   }
 
   // Partitions per tile and partial rows per split tile, for partition length P.
-  long long units_total = 0, unit_off = 0, prows_total = 0, prow_off = 0;
+  long long units_total = 0, prows_total = 0, prow_off = 0;
   for (;;) {
     long long units = 0, prows = 0;
     for (int s = s0; s < s1; ++s) {
@@ -137,13 +161,39 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
         if (np > 1) prows += np * min(RT, rows - tt * RT) * p.num_kv_heads;
       }
     }
-    unit_off = block_exclusive_scan(units, &units_total, sm);
+    block_exclusive_scan(units, &units_total, sm);
     prow_off = block_exclusive_scan(prows, &prows_total, sm);
     if ((units_total <= p.unit_cap && prows_total <= p.prow_cap) || P >= max_kmax) break;
     P *= 2;
   }
 
-  long long tb = tile_off, ub = unit_off, pr = prow_off;
+  // Counting sort of the units by stage count, longest first: histogram, bucket offsets, scatter.
+  for (int i = t; i < kSortBuckets; i += kPlanThreads) bucket[i] = 0;
+  __syncthreads();
+  for (int s = s0; s < s1; ++s) {
+    const int nt = p.buf.seq_tiles[s];
+    if (nt == 0) continue;
+    const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
+    const int rows = n * G;
+    for (int tt = 0; tt < nt; ++tt) {
+      const int km = tile_kmax(L, n, G, rows, RT, tt);
+      const int np = static_cast<int>((km + P - 1) / P);
+      for (int pp = 0; pp < np; ++pp) {
+        const int keys = static_cast<int>(min(static_cast<long long>(km) - pp * P, P));
+        atomicAdd(&bucket[sort_bucket(keys)], 1);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const long long c = t < kSortBuckets ? bucket[t] : 0;
+    long long dummy;
+    const long long off = block_exclusive_scan(c, &dummy, sm);
+    if (t < kSortBuckets) bucket[t] = static_cast<int>(off);
+  }
+  __syncthreads();
+
+  long long tb = tile_off, pr = prow_off;
   for (int s = s0; s < s1; ++s) {
     p.buf.tile_base[s] = static_cast<int>(tb);
     const int nt = p.buf.seq_tiles[s];
@@ -151,18 +201,20 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
     const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
     const int rows = n * G;
     for (int tt = 0; tt < nt; ++tt) {
-      const int np = static_cast<int>((tile_kmax(L, n, G, rows, RT, tt) + P - 1) / P);
+      const int km = tile_kmax(L, n, G, rows, RT, tt);
+      const int np = static_cast<int>((km + P - 1) / P);
       const int rows_t = min(RT, rows - tt * RT);
-      p.buf.tile_rec[tb] = make_int2(static_cast<int>(ub), np);
+      const int pb0 = np > 1 ? static_cast<int>(pr) : -1;
+      p.buf.tile_rec[tb] = make_int4(s, tt, pb0, np);
       ++tb;
       for (int pp = 0; pp < np; ++pp) {
-        int pb = -1;
-        if (np > 1) {
-          pb = static_cast<int>(pr);
-          pr += static_cast<long long>(rows_t) * p.num_kv_heads;
-        }
-        p.buf.units[ub++] = make_int4(s, tt, pp, pb);
+        const int keys = static_cast<int>(min(static_cast<long long>(km) - pp * P, P));
+        const int slot = atomicAdd(&bucket[sort_bucket(keys)], 1);
+        const int pb = np > 1 ? static_cast<int>(pr + static_cast<long long>(pp) * rows_t * p.num_kv_heads)
+                              : -1;
+        p.buf.units[slot] = make_int4(s, tt, pp, pb);
       }
+      if (np > 1) pr += static_cast<long long>(np) * rows_t * p.num_kv_heads;
     }
   }
   if (t == 0) {
@@ -176,36 +228,35 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
 }
 
 // One workgroup per (row tile, kv head).  Tiles with a single partition were finished by the main
-// kernel and are skipped.
+// kernel and are skipped.  Partition pp of a split tile with `rows` rows keeps kv head g's row r at
+// partial row pb0 + pp * rows * H_kv + g * rows + r.
 template <int D>
 __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams p) {
   const int tile_idx = blockIdx.x;
   const int g = blockIdx.y;
   if (tile_idx >= p.buf.hdr[kHdrTiles]) return;
-  const int2 rec = p.buf.tile_rec[tile_idx];
-  if (rec.y <= 1) return;
-  const int4 u = p.buf.units[rec.x];
-  const int s = u.x, tile = u.y;
+  const int4 rec = p.buf.tile_rec[tile_idx];
+  const int np = rec.w;
+  if (np <= 1) return;
+  const int s = rec.x, tile = rec.y, pb0 = rec.z;
   const int q0 = p.query_start_loc[s];
   const int n = p.query_start_loc[s + 1] - q0;
   const int G = p.group;
   const int RT = p.rows_per_tile;
   const int row0 = tile * RT;
   const int rows_here = min(RT, n * G - row0);
+  const int64_t part_stride = static_cast<int64_t>(rows_here) * p.num_kv_heads;
   constexpr int D4 = D / 4;
   for (int w = threadIdx.x; w < rows_here * D4; w += kThreads) {
     const int rl = w / D4;
     const int d0 = (w - rl * D4) * 4;
-    const int row_off = g * rows_here + rl;
+    const int64_t row_base = pb0 + static_cast<int64_t>(g) * rows_here + rl;
     float M = -INFINITY;
-    for (int pp = 0; pp < rec.y; ++pp) {
-      const int64_t prow = p.buf.units[rec.x + pp].w + row_off;
-      M = fmaxf(M, p.buf.part_ml[prow].x);
-    }
+    for (int pp = 0; pp < np; ++pp) M = fmaxf(M, p.buf.part_ml[row_base + pp * part_stride].x);
     const float mref = M == -INFINITY ? 0.f : M;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, den = 0.f;
-    for (int pp = 0; pp < rec.y; ++pp) {
-      const int64_t prow = p.buf.units[rec.x + pp].w + row_off;
+    for (int pp = 0; pp < np; ++pp) {
+      const int64_t prow = row_base + pp * part_stride;
       const float2 ml = p.buf.part_ml[prow];
       const float wgt = __builtin_amdgcn_exp2f(ml.x - mref);
       den += wgt * ml.y;

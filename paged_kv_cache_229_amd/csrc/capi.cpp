@@ -78,7 +78,7 @@ struct WsLayout {
 };
 
 int choose_tile_kind(int group, int64_t total_q, int32_t max_q_len_hint) {
-  if (g_tile_kind == 1 || g_tile_kind == 2) return g_tile_kind;
+  if (g_tile_kind == 1) return g_tile_kind;
   (void)group;
   (void)total_q;
   (void)max_q_len_hint;
@@ -89,7 +89,8 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
                           int32_t head_dim, int tile_kind) {
   WsLayout w{};
   const int group = num_q_heads / num_kv_heads;
-  w.rows_per_tile = pkv::kAttnWaves * 16 * (tile_kind == 2 ? 2 : 1);
+  (void)tile_kind;
+  w.rows_per_tile = pkv::kTileRows;
   // Each sequence adds at most one partly filled tile.
   w.tile_cap = (total_q * group + w.rows_per_tile - 1) / w.rows_per_tile + num_seqs;
   w.unit_cap = (pkv::kMaxItems + num_kv_heads - 1) / num_kv_heads + w.tile_cap;
@@ -103,7 +104,7 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   w.tile_base = off;
   off = round256(off + static_cast<size_t>(num_seqs + 1) * sizeof(int));
   w.tile_rec = off;
-  off = round256(off + static_cast<size_t>(w.tile_cap) * 2 * sizeof(int));
+  off = round256(off + static_cast<size_t>(w.tile_cap) * 4 * sizeof(int));
   w.units = off;
   off = round256(off + static_cast<size_t>(w.unit_cap) * 4 * sizeof(int));
   const size_t part_rows = pkv::kPartialRowCap;
@@ -261,7 +262,7 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
   b.seq_tiles = reinterpret_cast<int*>(ws + w.seq_tiles);
   b.seq_units = reinterpret_cast<int*>(ws + w.seq_units);
   b.tile_base = reinterpret_cast<int*>(ws + w.tile_base);
-  b.tile_rec = reinterpret_cast<int2*>(ws + w.tile_rec);
+  b.tile_rec = reinterpret_cast<int4*>(ws + w.tile_rec);
   b.units = reinterpret_cast<int4*>(ws + w.units);
   b.part_ml = reinterpret_cast<float2*>(ws + w.part_ml);
   b.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
@@ -301,8 +302,8 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
 }
 
 int paged_attention_set_tuning(int32_t partition_keys, int32_t target_items, int32_t tile_kind) {
-  if (partition_keys < 0 || target_items < 0 || tile_kind < 0 || tile_kind > 2)
-    return fail(PKV_ERR_INVALID_ARG, "tuning values must be >= 0 and tile_kind in {0, 1, 2}");
+  if (partition_keys < 0 || target_items < 0 || tile_kind < 0 || tile_kind > 1)
+    return fail(PKV_ERR_INVALID_ARG, "tuning values must be >= 0 and tile_kind in {0, 1}");
   if (target_items > pkv::kMaxItems)
     return fail(PKV_ERR_INVALID_ARG, "target_items must be <= " + std::to_string(pkv::kMaxItems));
   g_partition_keys = partition_keys;

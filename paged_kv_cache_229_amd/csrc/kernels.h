@@ -10,9 +10,10 @@ namespace pkv {
 // of it.
 constexpr int kStageKeys = 64;
 constexpr int kThreads = 256;
-// The bf16 attention workgroup: 8 waves (two per SIMD).
+// The bf16 attention workgroup: 8 waves (two per SIMD), 128-row tiles (16 rows per wave).
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kTileRows = 16 * kAttnWaves;
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
 constexpr int kDefaultItems = 1024;
@@ -28,7 +29,7 @@ struct PlanBuffers {
   int* seq_tiles;   // [num_seqs]  scratch
   int* seq_units;   // [num_seqs]  scratch
   int* tile_base;   // [num_seqs + 1] first tile record of each sequence
-  int2* tile_rec;   // [tile_cap]  {first unit, number of partitions}
+  int4* tile_rec;   // [tile_cap]  {sequence, tile, first partial row or -1, number of partitions}
   int4* units;      // [unit_cap]  {sequence, tile, partition, first partial row or -1 if unsplit}
   float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
   float* part_acc;  // [prow_cap * head_dim] unnormalised partial outputs
@@ -93,8 +94,7 @@ struct KvWriteParams {
 
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
-// tile_kind 1: 16 rows per wave (128-row tiles), 2: 32 rows per wave (256-row tiles).
-// grid = persistent workgroups.
+// grid = persistent workgroups; tile_kind is reserved (one tile shape today).
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
                                  hipStream_t stream);
 hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream);

@@ -130,6 +130,7 @@ def test_tuning_and_events_validation():
     lib = N.lib()
     assert lib.paged_attention_set_tuning(-1, 0, 0) == N.PKV_ERR_INVALID_ARG
     assert lib.paged_attention_set_tuning(0, 0, 3) == N.PKV_ERR_INVALID_ARG
+    assert lib.paged_attention_set_tuning(0, 0, 2) == N.PKV_ERR_INVALID_ARG
     assert lib.paged_attention_set_tuning(0, 1 << 20, 0) == N.PKV_ERR_INVALID_ARG
     assert lib.paged_attention_set_tuning(0, 0, 0) == N.PKV_OK
     assert lib.paged_attention_set_profile_events(FAKE, None) == N.PKV_ERR_INVALID_ARG

@@ -88,16 +88,19 @@ def test_forced_partitions(name, partition):
     check_close(out_f64(out), outs[0], BF16, f"{name} P={partition}")
 
 
+@pytest.mark.parametrize("items", [1, 7, 64, 4096])
 @pytest.mark.parametrize("name", ["decode", "mixed", "spec", "prefix"])
-def test_tile_kind_128(name):
+def test_item_counts(name, items):
+    """Few or many work items (one item per workgroup up to several rounds of the snake assignment, long
+    and short partitions) give the oracle's result."""
     w = make_config(name, "small")
-    log(f"small {name} tile_kind=2")
-    pkv.set_tuning(0, 0, 2)
+    log(f"small {name} target_items={items}")
+    pkv.set_tuning(0, items, 0)
     dw = DeviceWorkload(w)
     out = dw.run_step(0)
     _, _, outs = _oracle_steps(w)
     torch.cuda.synchronize()
-    check_close(out_f64(out), outs[0], BF16, f"{name} tile128")
+    check_close(out_f64(out), outs[0], BF16, f"{name} items={items}")
 
 
 @pytest.mark.parametrize("dtype", [BF16, FP32])
