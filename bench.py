@@ -158,6 +158,8 @@ def main() -> None:
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--items", type=int, default=0)
     ap.add_argument("--tile-kind", type=int, default=0)
+    ap.add_argument("--subset", choices=["all", "prefill", "decode"], default="all",
+                    help="time only the sequences with q_len > 1 (prefill) or q_len == 1 (decode)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -171,7 +173,7 @@ def main() -> None:
     import torch
 
     import paged_kv_cache_229_amd as pkv
-    from workloads import make_config
+    from workloads import make_config, subset_workload
 
     dev = torch.device("cuda", 0)
     if args.calibrate_copy:
@@ -185,6 +187,11 @@ def main() -> None:
         return
     t_gen = time.perf_counter()
     w = make_config(args.workload, "full")
+    if args.subset != "all":
+        qlens = np.diff(w.steps[0].query_start_loc)
+        keep = np.nonzero(qlens > 1 if args.subset == "prefill" else qlens == 1)[0]
+        w = subset_workload(w, keep)
+        w.description += f" [{args.subset} sequences only: {len(keep)}]"
     print(f"[bench] generated {w.description} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
     work = algorithmic_work(w)
@@ -250,7 +257,8 @@ def main() -> None:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "description": w.description, "num_seqs": w.num_seqs,
+        "config": {"workload": w.name, "subset": args.subset, "description": w.description,
+                   "num_seqs": w.num_seqs,
                    "total_q": work["total_q"], "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "pool_copies": len(copies)},
@@ -259,6 +267,7 @@ def main() -> None:
         "attention_kernel_ms": {"mean": round(k_avg, 5), "p10": round(float(np.percentile(kernel_ms, 10)), 5),
                                 "p90": round(float(np.percentile(kernel_ms, 90)), 5)},
         "attention_tflops": round(work["flops"] / (k_avg * 1e-3) / 1e12, 2),
+        "attention_pct_mfma_peak": round(100 * work["flops"] / (k_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
         "attention_logical_gbs": round(work["attn_bytes_logical"] / (k_avg * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),

@@ -417,8 +417,8 @@ hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kin
                                  hipStream_t stream) {
   (void)tile_kind;
   const dim3 g(static_cast<unsigned>(grid)), b(kAttnThreads);
-  if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);
-  else hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), g, b, 0, stream, p);
+  if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaveNTiles>), g, b, 0, stream, p);
+  else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaveNTiles>), g, b, 0, stream, p);
   return hipGetLastError();
 }
 

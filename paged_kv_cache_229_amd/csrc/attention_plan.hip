@@ -227,11 +227,14 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
   }
 }
 
-// One workgroup per (row tile, kv head).  Tiles with a single partition were finished by the main
-// kernel and are skipped.  Partition pp of a split tile with `rows` rows keeps kv head g's row r at
-// partial row pb0 + pp * rows * H_kv + g * rows + r.
+// One thread per (row, 4 channels) of a split tile: workgroup (tile, kv head, block of rows).  Tiles with
+// a single partition were finished by the main kernel and are skipped.  Partition pp of a split tile with
+// `rows` rows keeps kv head g's row r at partial row pb0 + pp * rows * H_kv + g * rows + r.  The
+// partitions are folded in one pass with a running maximum, loads unrolled so they overlap.
 template <int D>
 __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams p) {
+  constexpr int D4 = D / 4;
+  constexpr int RPW = kThreads / D4;  // rows per workgroup
   const int tile_idx = blockIdx.x;
   const int g = blockIdx.y;
   if (tile_idx >= p.buf.hdr[kHdrTiles]) return;
@@ -245,41 +248,41 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
   const int RT = p.rows_per_tile;
   const int row0 = tile * RT;
   const int rows_here = min(RT, n * G - row0);
+  const int rl = blockIdx.z * RPW + threadIdx.x / D4;
+  if (rl >= rows_here) return;
+  const int d0 = (threadIdx.x % D4) * 4;
   const int64_t part_stride = static_cast<int64_t>(rows_here) * p.num_kv_heads;
-  constexpr int D4 = D / 4;
-  for (int w = threadIdx.x; w < rows_here * D4; w += kThreads) {
-    const int rl = w / D4;
-    const int d0 = (w - rl * D4) * 4;
-    const int64_t row_base = pb0 + static_cast<int64_t>(g) * rows_here + rl;
-    float M = -INFINITY;
-    for (int pp = 0; pp < np; ++pp) M = fmaxf(M, p.buf.part_ml[row_base + pp * part_stride].x);
-    const float mref = M == -INFINITY ? 0.f : M;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, den = 0.f;
-    for (int pp = 0; pp < np; ++pp) {
-      const int64_t prow = row_base + pp * part_stride;
-      const float2 ml = p.buf.part_ml[prow];
-      const float wgt = __builtin_amdgcn_exp2f(ml.x - mref);
-      den += wgt * ml.y;
-      const float4 a = *reinterpret_cast<const float4*>(p.buf.part_acc + prow * D + d0);
-      a0 += wgt * a.x;
-      a1 += wgt * a.y;
-      a2 += wgt * a.z;
-      a3 += wgt * a.w;
-    }
-    const float inv = 1.f / den;
-    const int r = row0 + rl;
-    const int i = r / G;
-    const int hh = r - i * G;
-    __bf16* o = static_cast<__bf16*>(p.out) +
-                ((static_cast<int64_t>(q0 + i) * p.num_q_heads + g * G + hh) * D + d0);
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 v;
-    v[0] = static_cast<__bf16>(a0 * inv);
-    v[1] = static_cast<__bf16>(a1 * inv);
-    v[2] = static_cast<__bf16>(a2 * inv);
-    v[3] = static_cast<__bf16>(a3 * inv);
-    *reinterpret_cast<bf16x4*>(o) = v;
+  const int64_t row_base = pb0 + static_cast<int64_t>(g) * rows_here + rl;
+  float M = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 4
+  for (int pp = 0; pp < np; ++pp) {
+    const int64_t prow = row_base + pp * part_stride;
+    const float2 ml = p.buf.part_ml[prow];
+    const float4 a = *reinterpret_cast<const float4*>(p.buf.part_acc + prow * D + d0);
+    const float mnew = fmaxf(M, ml.x);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float s_old = __builtin_amdgcn_exp2f(M - mref);
+    const float s_new = __builtin_amdgcn_exp2f(ml.x - mref);
+    den = den * s_old + ml.y * s_new;
+    a0 = a0 * s_old + a.x * s_new;
+    a1 = a1 * s_old + a.y * s_new;
+    a2 = a2 * s_old + a.z * s_new;
+    a3 = a3 * s_old + a.w * s_new;
+    M = mnew;
   }
+  const float inv = 1.f / den;
+  const int r = row0 + rl;
+  const int i = r / G;
+  const int hh = r - i * G;
+  __bf16* o = static_cast<__bf16*>(p.out) +
+              ((static_cast<int64_t>(q0 + i) * p.num_q_heads + g * G + hh) * D + d0);
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v;
+  v[0] = static_cast<__bf16>(a0 * inv);
+  v[1] = static_cast<__bf16>(a1 * inv);
+  v[2] = static_cast<__bf16>(a2 * inv);
+  v[3] = static_cast<__bf16>(a3 * inv);
+  *reinterpret_cast<bf16x4*>(o) = v;
 }
 
 }  // namespace
@@ -291,7 +294,9 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
 
 hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream) {
   if (tile_cap <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(tile_cap), static_cast<unsigned>(p.num_kv_heads));
+  const int rows_per_wg = kThreads / (head_dim / 4);
+  const dim3 grid(static_cast<unsigned>(tile_cap), static_cast<unsigned>(p.num_kv_heads),
+                  static_cast<unsigned>((kTileRows + rows_per_wg - 1) / rows_per_wg));
   if (head_dim == 128) {
     hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(kThreads), 0, stream, p);
   } else {

@@ -10,10 +10,12 @@ namespace pkv {
 // of it.
 constexpr int kStageKeys = 64;
 constexpr int kThreads = 256;
-// The bf16 attention workgroup: 8 waves (two per SIMD), 128-row tiles (16 rows per wave).
+// The bf16 attention workgroup: 8 waves (two per SIMD); each wave owns kWaveNTiles 16-row n-tiles, so a
+// tile has 128 rows.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kTileRows = 16 * kAttnWaves;
+constexpr int kWaveNTiles = 1;
+constexpr int kTileRows = 16 * kWaveNTiles * kAttnWaves;
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
 constexpr int kDefaultItems = 1024;

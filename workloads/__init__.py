@@ -18,5 +18,6 @@ from .synth import (  # noqa: F401
     config_spec,
     config_tiny,
     make_config,
+    subset_workload,
     CONFIG_NAMES,
 )

@@ -324,3 +324,25 @@ def make_config(name: str, size: str = "full", dtype: str | None = None) -> Work
     if name == "prefix":
         return config_prefix(seed=229105, num_seqs=12, shared_blocks=8, suffix_range=(1, 300), **kw)
     raise ValueError(name)
+
+
+def subset_workload(w: Workload, seqs) -> Workload:
+    """The same pool and step restricted to the sequences `seqs` (in that order): their table rows,
+    lengths, query rows, new K/V rows and slots.  Used to time the prefill or decode part of a mixed step
+    on its own."""
+    seqs = [int(s) for s in seqs]
+    out_steps = []
+    for st in w.steps:
+        qsl = st.query_start_loc
+        rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs]).astype(np.int64)
+        q_lens = np.array([qsl[s + 1] - qsl[s] for s in seqs], dtype=np.int64)
+        new_qsl = np.zeros(len(seqs) + 1, dtype=np.int32)
+        new_qsl[1:] = np.cumsum(q_lens)
+        out_steps.append(Step(q=st.q[rows], k_new=st.k_new[rows], v_new=st.v_new[rows],
+                              slot_mapping=st.slot_mapping[rows], context_lens=st.context_lens[seqs],
+                              query_start_loc=new_qsl))
+    return Workload(name=w.name, dtype=w.dtype, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                    head_dim=w.head_dim, block_size=w.block_size, num_blocks=w.num_blocks,
+                    block_tables=w.block_tables[seqs], k_pool=w.k_pool, v_pool=w.v_pool, steps=out_steps,
+                    scale=w.scale, shared_prefix_blocks=w.shared_prefix_blocks,
+                    description=w.description)
