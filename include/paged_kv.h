@@ -110,7 +110,8 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int64_t total_q, int32_t
  *   context_lens  (device) [num_seqs] int32
  *   query_start_loc (device) [num_seqs + 1] int32, query_start_loc[0] == 0, query_start_loc[num_seqs]
  *                 == total_q; a sequence with n == 0 is skipped
- *   scale         multiplies Q K^T before the mask and the softmax (natural exponential)
+ *   scale         multiplies Q K^T before the mask and the softmax (natural exponential); must be
+ *                 finite and > 0 (a softmax temperature), else PKV_ERR_INVALID_ARG
  *   max_q_len_hint  an upper bound on n over the batch, or <= 0 if unknown (picks the row tile)
  *   workspace     (device) scratch of at least paged_attention_workspace_size() bytes, 256-byte aligned;
  *                 its contents need no initialisation and are meaningless after the call.  Calls that
@@ -134,7 +135,8 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
  *                   multiple of 128); 0 = chosen per call from the lengths on the device.
  *   target_items    > 0: aim the automatic choice at this many (tile, kv head, partition) work items;
  *                   0 = default.
- *   tile_kind       0 = automatic; 1 = 128-row tiles (the only tile shape of this version).
+ *   tile_kind       0 = automatic: 1 when max_q_len_hint * (num_q_heads / num_kv_heads) <= 128,
+ *                   else 2; 1 = 128-row tiles (16 rows per wave); 2 = 256-row tiles (32 rows per wave).
  */
 int paged_attention_set_tuning(int32_t partition_keys, int32_t target_items, int32_t tile_kind);
 

@@ -37,6 +37,12 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The bf16 attention kernel compares raw MFMA scores with fmaxf; without NaN
+# semantics those become plain v_max3_f32 (no canonicalising copies).  NaN inputs give NaN or unspecified
+# output either way.
+EXTRA_FLAGS = {"attention_bf16.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -46,7 +52,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -31,6 +31,8 @@
 //    few (decode); in the latter case the waves' softmax states are merged through LDS at the end.
 //  * A tile whose context was split into partitions writes (acc, m, l) per row; split_reduce_kernel
 //    merges them.  Unsplit tiles write the normalised bf16 output directly.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace pkv {
@@ -74,6 +76,20 @@ __device__ inline void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Maximum over the four lanes l % 16 + 16 * {0, 1, 2, 3} (the lanes holding one row's scores): a swap of
+// the wave halves, then of neighbouring 16-lane rows, each followed by a max of the two copies.
+__device__ inline float row_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// A row's reference maximum (log2 units) moves only when a chunk's maximum exceeds it by more than this,
+// so probabilities stay below 2^kLazyRescale and the accumulator is rescaled rarely; acc, l and m stay
+// mutually consistent, so the normalised result is unchanged.
+constexpr float kLazyRescale = 8.f;
+
 // 16-byte-chunk swizzle of LDS row `key`.
 template <int D>
 __device__ inline int k_swizzle(int key) {
@@ -91,21 +107,23 @@ struct Geo {
   static constexpr int DT = D / 16;          // 16-channel output tiles
   static constexpr int WROWS = 16 * NTW;     // rows one wave owns
   static constexpr int RT = NW * WROWS;      // rows per tile
-  static_assert(RT == kTileRows, "the plan and the kernel agree on the tile height");
+  static_assert(RT == tile_rows_of(NTW), "the plan and the kernel agree on the tile height");
   static constexpr int ROWB = 2 * D;         // bytes of one key row in LDS
   static constexpr int TILEB = kStageKeys * ROWB;
   static constexpr int STAGEB = 2 * TILEB;   // K tile + V tile
   static constexpr int NBUF = 4;
   static constexpr int LDS = NBUF * STAGEB;
   static constexpr int MERGE_SLOT = DT * 256 + 32;  // floats per (wave, n-tile) in the merge buffer
-  static_assert((NW - 1) * NTW * MERGE_SLOT * 4 <= LDS, "merge buffer must fit the ring");
+  static constexpr int MERGE_BYTES = NW * NTW * MERGE_SLOT * 4;
+  static constexpr int SMEM = LDS > MERGE_BYTES ? LDS : MERGE_BYTES;  // ring, later reused for the merge
   static_assert(NL >= 1 && KPW % KPL == 0, "stage split");
 };
 
 template <int D, int NTW>
-__global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_kernel(const AttnParams p) {
   using T = Geo<D, NTW>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[T::SMEM];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
@@ -135,9 +153,27 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
   const int tr_key = 4 * g4 + (l16 >> 2);
   const int tr_half = (l16 & 1) << 3;       // byte offset inside the 16-byte chunk
   const int tr_chunk = (l16 & 3) >> 1;      // chunk offset inside the 16-channel tile
+  // Byte offsets of the lane's fragment reads inside a stage, for key group 0; other key groups (+16,
+  // +32, +48 keys) add a constant, because the swizzle depends on the key modulo 16 only.
+  int koff[T::DC];  // K: key l16, 16-byte chunk 4*dc + g4 (A operand of S^T = K Q^T)
+  int voff[T::DT];  // V: transpose-read row of tile dt (A operand of O^T += V^T P^T)
+#pragma unroll
+  for (int dc = 0; dc < T::DC; ++dc) koff[dc] = l16 * T::ROWB + (((4 * dc + g4) ^ k_swizzle<D>(l16)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt)
+    voff[dt] = T::TILEB + tr_key * T::ROWB + tr_half + (((2 * dt + tr_chunk) ^ k_swizzle<D>(tr_key)) << 4);
+  // bf16 ones: A operand that turns an MFMA over P^T into the row sums of P.
+  bf16x8 ones;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ones[t] = static_cast<__bf16>(1.f);
+  const float inv_sl2 = 1.f / sl2;
 
+  // The next item is claimed while the current one finishes (after its last stage), so the atomic's
+  // latency hides behind the epilogue.
+  int next_item = 0;
+  if (tid == 0) next_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
+    if (tid == 0) s_item = next_item;
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     __syncthreads();
@@ -162,6 +198,13 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
     const int wr = wave / WK;
     const int wk = wave - wr * WK;
     const int my_row0 = row0 + wr * T::WROWS;
+    // 16-row n-tiles of this wave that hold rows of the item (0 when the last row group is empty).
+    const int ntv = min(NTW, (row0 + rows_here - my_row0 + 15) >> 4);
+    // Last visible key of the wave's first row: chunks ending at or before it need no mask for any row
+    // of the wave (rows are ordered by query token, whose visible range only grows).
+    const int lim0 = min(L - n + my_row0 / G, ke - 1);
+    // Last visible key of the wave's last row: later chunks are masked for the whole wave and skipped.
+    const int limw = min(L - n + (min(my_row0 + 16 * ntv, row0 + rows_here) - 1) / G, ke - 1);
     const CONST_AS int* const tbl =
         (const CONST_AS int*)(p.block_tables + static_cast<int64_t>(s) * p.max_blocks_per_seq);
     const int nst = (ke - kb + kStageKeys - 1) / kStageKeys;
@@ -228,14 +271,106 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
     if (nst > 2) issue(2, tb2);
 
     f32x4 acc[NTW][T::DT];
-    float m[NTW], lsum[NTW];
+    f32x4 lacc[NTW];   // row sums of P, accumulated by MFMA (all four entries equal)
+    float m[NTW];      // reference maximum of the row's scaled scores (log2 units)
+    float thr[NTW];    // raw score above which m must move: (m + kLazyRescale) / (scale log2 e)
+    float nmr[NTW];    // -m, or 0 while m is -inf
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       m[nt] = -INFINITY;
-      lsum[nt] = 0.f;
+      thr[nt] = -INFINITY;
+      nmr[nt] = 0.f;
+      lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+
+    // One 32-key chunk (keys kc0 + [0, 32) at rows 32c .. 32c+31 of the stage tiles) for the wave's first
+    // NA n-tiles.  kp / vp: the lane's K / V read addresses in the current stage for key group 0.
+    auto chunk = [&](auto na_tag, const unsigned char* const* kp, const unsigned char* const* vp, int c,
+                     int kc0) __attribute__((always_inline)) {
+      constexpr int NA = decltype(na_tag)::value;
+      // S^T for keys 32c + 16mt + [0, 16), mt = 0, 1.
+      f32x4 sacc[NA][2];
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) sacc[nt][0] = sacc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int dc = 0; dc < T::DC; ++dc) {
+          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kp[dc] + (32 * c + 16 * mt) * T::ROWB));
+#pragma unroll
+          for (int nt = 0; nt < NA; ++nt) sacc[nt][mt] = mfma_qk(kf, qf[nt][dc], sacc[nt][mt]);
+        }
+      }
+      // V^T operands of this chunk, read now so that their LDS latency hides behind the softmax.
+      bf16x8 vf[T::DT];
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[dt] + 32 * c * T::ROWB));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp[dt] + (32 * c + 16) * T::ROWB));
+        vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      // Online softmax over the 32 keys; the lane holds keys kc0 + 4*g4 + 16*mt + [0, 4) of row l16.
+      // Raw scores are compared (the scale is positive) and the scale is applied inside the exponent.
+      float sv[NA][8];
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt)
+#pragma unroll
+        for (int k8 = 0; k8 < 8; ++k8) sv[nt][k8] = sacc[nt][k8 >> 2][k8 & 3];
+      if (kc0 + 31 > lim0) {  // the chunk reaches past some row's last visible key
+        const int kl = kc0 + 4 * g4;
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt)
+#pragma unroll
+          for (int k8 = 0; k8 < 8; ++k8)
+            sv[nt][k8] = (kl + 16 * (k8 >> 2) + (k8 & 3) <= lim[nt]) ? sv[nt][k8] : -INFINITY;
+      }
+      // Lane-local maxima; only when one exceeds its row's threshold are the rows' maxima formed and the
+      // references moved (rare after the first chunk).
+      float lm[NA];
+      bool grow = false;
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) {
+        float x = sv[nt][0];
+#pragma unroll
+        for (int k8 = 1; k8 < 8; ++k8) x = fmaxf(x, sv[nt][k8]);
+        lm[nt] = x;
+        grow |= x > thr[nt];
+      }
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt) {
+          const float mnew = fmaxf(m[nt], row_max4(lm[nt]) * sl2);
+          if (mnew != -INFINITY) {
+            const float alpha = __builtin_amdgcn_exp2f(m[nt] - mnew);
+            lacc[nt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < T::DT; ++dt) acc[nt][dt] *= alpha;
+            m[nt] = mnew;
+            nmr[nt] = -mnew;
+            thr[nt] = (mnew + kLazyRescale) * inv_sl2;
+          }
+        }
+      }
+      bf16x8 pf[NA];
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt)
+#pragma unroll
+        for (int k8 = 0; k8 < 8; ++k8)
+          pf[nt][k8] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][k8], sl2, nmr[nt])));
+      // O^T += V^T P^T over the 32 keys (v_mfma_f32_16x16x32_bf16): the contraction index 8*g4 + t is key
+      // 4*g4 + t of the first 16-key half for t < 4 and of the second half for t >= 4, which is where the
+      // S^T fragments put the probabilities; one transpose read per half gives the matching V^T operand.
+      // The row sums of the same bf16 probabilities come from one more MFMA against ones.
+#pragma unroll
+      for (int nt = 0; nt < NA; ++nt) lacc[nt] = mfma_qk(ones, pf[nt], lacc[nt]);
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < NA; ++nt) acc[nt][dt] = mfma_qk(vf[dt], pf[nt], acc[nt][dt]);
+    };
 
     for (int st = 0; st < nst; ++st) {
       // Stage st has landed once at most the later stages' loads are outstanding.
@@ -246,157 +381,96 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
       __syncthreads();  // all waves' loads of stage st landed; all waves done with stage st-1
       if (st + 3 < nst) issue(st + 3, tbn);
 
-      const unsigned char* const Ks = smem + (st & (T::NBUF - 1)) * T::STAGEB;
-      const unsigned char* const Vs = Ks + T::TILEB;
+      const unsigned char* const stage = smem + (st & (T::NBUF - 1)) * T::STAGEB;
+      const unsigned char* kp[T::DC];
+      const unsigned char* vp[T::DT];
+#pragma unroll
+      for (int dc = 0; dc < T::DC; ++dc) kp[dc] = stage + koff[dc];
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) vp[dt] = stage + voff[dt];
       const int kstage = kb + st * kStageKeys;
       // Two 32-key chunks per stage; chunk number st*2+c goes to the key-group (st*2+c) % WK.
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if (((st * 2 + c) % WK) != wk || kstage + 32 * c >= ke) continue;
-        // S^T for keys 32c + 16mt + [0, 16), mt = 0, 1.
-        f32x4 sacc[NTW][2];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) sacc[nt][0] = sacc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int key = 32 * c + 16 * mt + l16;
-#pragma unroll
-          for (int dc = 0; dc < T::DC; ++dc) {
-            const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                Ks + key * T::ROWB + (((4 * dc + g4) ^ k_swizzle<D>(key)) << 4)));
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) sacc[nt][mt] = mfma_qk(kf, qf[nt][dc], sacc[nt][mt]);
-          }
-        }
-        // Online softmax over the 32 keys; the lane holds keys kabs0 + 16*mt + [0, 4) of row l16.
-        const int kabs0 = kstage + 32 * c + 4 * g4;
-        bf16x8 pf[NTW];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          float sv[8];
-          float cm = -INFINITY;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const float x = sacc[nt][mt][jj] * sl2;
-              const float y = (kabs0 + 16 * mt + jj <= lim[nt]) ? x : -INFINITY;
-              sv[4 * mt + jj] = y;
-              cm = fmaxf(cm, y);
-            }
-          }
-          cm = fmaxf(cm, __shfl_xor(cm, 16));
-          cm = fmaxf(cm, __shfl_xor(cm, 32));
-          const float mnew = fmaxf(m[nt], cm);
-          const float mref = mnew == -INFINITY ? 0.f : mnew;
-          const float alpha = __builtin_amdgcn_exp2f(m[nt] - mref);
-          float ps = 0.f;
-#pragma unroll
-          for (int k8 = 0; k8 < 8; ++k8) {
-            const float pv = __builtin_amdgcn_exp2f(sv[k8] - mref);
-            ps += pv;
-            pf[nt][k8] = static_cast<__bf16>(pv);
-          }
-          lsum[nt] = lsum[nt] * alpha + ps;
-          m[nt] = mnew;
-#pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) acc[nt][dt] *= alpha;
-        }
-        // O^T += V^T P^T over the 32 keys (v_mfma_f32_16x16x32_bf16): the contraction index 8*g4 + t is key
-        // 4*g4 + t of the first 16-key half for t < 4 and of the second half for t >= 4, which is where the
-        // S^T fragments put the probabilities; one transpose read per half gives the matching V^T operand.
-        {
-          const int key_a = 32 * c + tr_key;
-          const int key_b = key_a + 16;
-          const unsigned char* const va = Vs + key_a * T::ROWB + tr_half;
-          const unsigned char* const vb = Vs + key_b * T::ROWB + tr_half;
-          const int swa = k_swizzle<D>(key_a);
-          const int swb = k_swizzle<D>(key_b);
-#pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_AS i16x4*)(va + (((2 * dt + tr_chunk) ^ swa) << 4)));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_AS i16x4*)(vb + (((2 * dt + tr_chunk) ^ swb) << 4)));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) acc[nt][dt] = mfma_qk(vf, pf[nt], acc[nt][dt]);
-          }
-        }
+        const int kc0 = kstage + 32 * c;
+        if (((st * 2 + c) % WK) != wk || kc0 > limw) continue;
+        if (NTW > 1 && ntv == NTW) chunk(std::integral_constant<int, NTW>{}, kp, vp, c, kc0);
+        else if (ntv > 0) chunk(std::integral_constant<int, 1>{}, kp, vp, c, kc0);
       }
       if (st + 4 < nst) fetch_table(st + 4, tbn);
     }
 
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      lsum[nt] += __shfl_xor(lsum[nt], 16);
-      lsum[nt] += __shfl_xor(lsum[nt], 32);
-    }
+    if (tid == 0) next_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
 
-    if (WK > 1) {  // waves that split the keys merge their softmax states through LDS
-      __syncthreads();
+    float lsum[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) lsum[nt] = lacc[nt][0];
+
+    // Writes d-tile dt of the lane's row in n-tile nt: the normalised bf16 output, or for a split tile
+    // the partial (acc, and with_ml: m and l).
+    auto emit = [&](int nt, int dt, f32x4 a, float mm, float ll, bool with_ml) __attribute__((always_inline)) {
+      const int r = my_row0 + nt * 16 + l16;
+      if (r >= row0 + rows_here) return;
+      if (pbase < 0) {
+        const int i = r / G;
+        const int hh = r - i * G;
+        const float inv = 1.f / ll;
+        bf16x4 v;
+        v[0] = static_cast<__bf16>(a[0] * inv);
+        v[1] = static_cast<__bf16>(a[1] * inv);
+        v[2] = static_cast<__bf16>(a[2] * inv);
+        v[3] = static_cast<__bf16>(a[3] * inv);
+        *reinterpret_cast<bf16x4*>(og + ((static_cast<int64_t>(q0 + i) * Hq + g * G + hh) * D + 4 * g4 + 16 * dt)) = v;
+      } else {
+        const int64_t prow = static_cast<int64_t>(pbase) + g * rows_here + (r - row0);
+        *reinterpret_cast<f32x4*>(p.buf.part_acc + prow * D + 4 * g4 + 16 * dt) = a;
+        if (with_ml && g4 == 0) p.buf.part_ml[prow] = make_float2(mm, ll);
+      }
+    };
+
+    if (WK == 1) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) emit(nt, dt, acc[nt][dt], m[nt], lsum[nt], dt == 0);
+    } else {
+      // The WK waves of a row group split the keys: each publishes its (acc, m, l) in LDS, then wave
+      // (wr, wk) combines d-tiles wk, wk + WK, ... of all WK states, so the merge is spread over the waves.
+      __syncthreads();  // every wave is done with the ring
       float* const mb = reinterpret_cast<float*>(smem);
-      if (wk > 0) {
-        float* const base = mb + ((wr * (WK - 1) + (wk - 1)) * NTW) * T::MERGE_SLOT;
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          float* const b = base + nt * T::MERGE_SLOT;
-#pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(b + dt * 256 + lane * 4) = acc[nt][dt];
-          if (g4 == 0) {
-            b[T::DT * 256 + 2 * l16] = m[nt];
-            b[T::DT * 256 + 2 * l16 + 1] = lsum[nt];
-          }
-        }
-      }
-      __syncthreads();
-      if (wk == 0) {
-        for (int o = 1; o < WK; ++o) {
-          const float* const base = mb + ((wr * (WK - 1) + (o - 1)) * NTW) * T::MERGE_SLOT;
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) {
-            const float* const b = base + nt * T::MERGE_SLOT;
-            const float mo = b[T::DT * 256 + 2 * l16];
-            const float lo = b[T::DT * 256 + 2 * l16 + 1];
-            const float mnew = fmaxf(m[nt], mo);
-            const float mref = mnew == -INFINITY ? 0.f : mnew;
-            const float a = __builtin_amdgcn_exp2f(m[nt] - mref);
-            const float bb = __builtin_amdgcn_exp2f(mo - mref);
-            lsum[nt] = lsum[nt] * a + lo * bb;
-            m[nt] = mnew;
-#pragma unroll
-            for (int dt = 0; dt < T::DT; ++dt)
-              acc[nt][dt] = acc[nt][dt] * a + *reinterpret_cast<const f32x4*>(b + dt * 256 + lane * 4) * bb;
-          }
-        }
-      }
-    }
-
-    if (wk == 0) {
+      float* const grp = mb + (wr * WK * NTW) * T::MERGE_SLOT;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        const int r = my_row0 + nt * 16 + l16;
-        if (r >= row0 + rows_here) continue;
-        if (pbase < 0) {
-          const int i = r / G;
-          const int hh = r - i * G;
-          const float inv = 1.f / lsum[nt];
-          __bf16* const o = og + ((static_cast<int64_t>(q0 + i) * Hq + g * G + hh) * D + 4 * g4);
+        if (nt >= ntv) break;  // only n-tiles with rows are merged
+        float* const b = grp + (wk * NTW + nt) * T::MERGE_SLOT;
 #pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) {
-            bf16x4 v;
-            v[0] = static_cast<__bf16>(acc[nt][dt][0] * inv);
-            v[1] = static_cast<__bf16>(acc[nt][dt][1] * inv);
-            v[2] = static_cast<__bf16>(acc[nt][dt][2] * inv);
-            v[3] = static_cast<__bf16>(acc[nt][dt][3] * inv);
-            *reinterpret_cast<bf16x4*>(o + 16 * dt) = v;
+        for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(b + dt * 256 + lane * 4) = acc[nt][dt];
+        if (g4 == 0) {
+          b[T::DT * 256 + 2 * l16] = m[nt];
+          b[T::DT * 256 + 2 * l16 + 1] = lsum[nt];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        if (nt >= ntv) break;
+        const float* const st0 = grp + nt * T::MERGE_SLOT + T::DT * 256 + 2 * l16;  // (m, l) of partner 0
+        float M = -INFINITY;
+        for (int o = 0; o < WK; ++o) M = fmaxf(M, st0[o * NTW * T::MERGE_SLOT]);
+        const float Mr = M == -INFINITY ? 0.f : M;
+        float Lsum = 0.f;
+        for (int o = 0; o < WK; ++o) {
+          const float* const so = st0 + o * NTW * T::MERGE_SLOT;
+          Lsum += so[1] * __builtin_amdgcn_exp2f(so[0] - Mr);
+        }
+        for (int dt = wk; dt < T::DT; dt += WK) {
+          f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int o = 0; o < WK; ++o) {
+            const float* const so = st0 + o * NTW * T::MERGE_SLOT;
+            a += *reinterpret_cast<const f32x4*>(grp + (o * NTW + nt) * T::MERGE_SLOT + dt * 256 + lane * 4) *
+                 __builtin_amdgcn_exp2f(so[0] - Mr);
           }
-        } else {
-          const int64_t prow = static_cast<int64_t>(pbase) + g * rows_here + (r - row0);
-          float* const pa = p.buf.part_acc + prow * D + 4 * g4;
-#pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(pa + 16 * dt) = acc[nt][dt];
-          if (g4 == 0) p.buf.part_ml[prow] = make_float2(m[nt], lsum[nt]);
+          emit(nt, dt, a, M, Lsum, dt == 0);
         }
       }
     }
@@ -406,19 +480,24 @@ __global__ void __launch_bounds__(kAttnThreads) attn_bf16_kernel(const AttnParam
 }  // namespace
 
 int attention_bf16_wgs_per_cu(int head_dim, int tile_kind) {
-  (void)tile_kind;
-  // 160 KiB of LDS per CU; the ring is 4 stages x 64 keys x (K + V) x head_dim x 2 bytes.
-  const int lds = 4 * 2 * kStageKeys * head_dim * 2 + 64;
+  // 160 KiB of LDS per CU; a workgroup holds the 4-stage K/V ring (reused for the merge) plus a word.
+  const int smem = tile_kind == 1 ? (head_dim == 128 ? Geo<128, 1>::SMEM : Geo<64, 1>::SMEM)
+                                  : (head_dim == 128 ? Geo<128, 2>::SMEM : Geo<64, 2>::SMEM);
+  const int lds = smem + 64;
   int wgs = (160 * 1024) / lds;
   return wgs < 1 ? 1 : (wgs > 2 ? 2 : wgs);
 }
 
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
                                  hipStream_t stream) {
-  (void)tile_kind;
   const dim3 g(static_cast<unsigned>(grid)), b(kAttnThreads);
-  if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, kWaveNTiles>), g, b, 0, stream, p);
-  else hipLaunchKernelGGL((attn_bf16_kernel<64, kWaveNTiles>), g, b, 0, stream, p);
+  if (tile_kind == 1) {
+    if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), g, b, 0, stream, p);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), g, b, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

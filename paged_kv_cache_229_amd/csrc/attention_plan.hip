@@ -296,7 +296,7 @@ hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, 
   if (tile_cap <= 0) return hipSuccess;
   const int rows_per_wg = kThreads / (head_dim / 4);
   const dim3 grid(static_cast<unsigned>(tile_cap), static_cast<unsigned>(p.num_kv_heads),
-                  static_cast<unsigned>((kTileRows + rows_per_wg - 1) / rows_per_wg));
+                  static_cast<unsigned>((kMaxTileRows + rows_per_wg - 1) / rows_per_wg));
   if (head_dim == 128) {
     hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(kThreads), 0, stream, p);
   } else {

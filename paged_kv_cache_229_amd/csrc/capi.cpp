@@ -77,20 +77,19 @@ struct WsLayout {
   int64_t tile_cap, unit_cap;
 };
 
+// Tile kind 1 (128-row tiles) when the hint says every sequence's rows (q_len x group) fit one such
+// tile; otherwise (long query chunks, or no hint) kind 2 (256-row tiles).  Only speed depends on it.
 int choose_tile_kind(int group, int64_t total_q, int32_t max_q_len_hint) {
-  if (g_tile_kind == 1) return g_tile_kind;
-  (void)group;
+  if (g_tile_kind > 0) return g_tile_kind;
   (void)total_q;
-  (void)max_q_len_hint;
-  return 1;
+  return (max_q_len_hint > 0 && static_cast<int64_t>(max_q_len_hint) * group <= pkv::tile_rows_of(1)) ? 1 : 2;
 }
 
 WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int tile_kind) {
   WsLayout w{};
   const int group = num_q_heads / num_kv_heads;
-  (void)tile_kind;
-  w.rows_per_tile = pkv::kTileRows;
+  w.rows_per_tile = pkv::tile_rows_of(tile_kind);
   // Each sequence adds at most one partly filled tile.
   w.tile_cap = (total_q * group + w.rows_per_tile - 1) / w.rows_per_tile + num_seqs;
   w.unit_cap = (pkv::kMaxItems + num_kv_heads - 1) / num_kv_heads + w.tile_cap;
@@ -209,7 +208,7 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
   if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size must be < 2^31");
-  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
   const int group = num_q_heads / num_kv_heads;
   if (total_q * group > INT32_MAX / 2 || total_q * num_q_heads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "total_q too large for one call");
@@ -302,8 +301,8 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
 }
 
 int paged_attention_set_tuning(int32_t partition_keys, int32_t target_items, int32_t tile_kind) {
-  if (partition_keys < 0 || target_items < 0 || tile_kind < 0 || tile_kind > 1)
-    return fail(PKV_ERR_INVALID_ARG, "tuning values must be >= 0 and tile_kind in {0, 1}");
+  if (partition_keys < 0 || target_items < 0 || tile_kind < 0 || tile_kind > 2)
+    return fail(PKV_ERR_INVALID_ARG, "tuning values must be >= 0 and tile_kind in {0, 1, 2}");
   if (target_items > pkv::kMaxItems)
     return fail(PKV_ERR_INVALID_ARG, "target_items must be <= " + std::to_string(pkv::kMaxItems));
   g_partition_keys = partition_keys;

@@ -10,12 +10,13 @@ namespace pkv {
 // of it.
 constexpr int kStageKeys = 64;
 constexpr int kThreads = 256;
-// The bf16 attention workgroup: 8 waves (two per SIMD); each wave owns kWaveNTiles 16-row n-tiles, so a
-// tile has 128 rows.
+// The bf16 attention workgroup: 8 waves (two per SIMD).  Tile kind k: each wave owns k 16-row n-tiles,
+// so a tile has 128 (kind 1) or 256 (kind 2) rows.  Kind 1 suits rows-poor batches (decode, speculative
+// decode), kind 2 long query chunks, where each K/V fragment read from LDS then feeds two MFMAs.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kWaveNTiles = 1;
-constexpr int kTileRows = 16 * kWaveNTiles * kAttnWaves;
+constexpr int tile_rows_of(int kind) { return 16 * kind * kAttnWaves; }
+constexpr int kMaxTileRows = tile_rows_of(2);
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
 constexpr int kDefaultItems = 1024;

@@ -97,6 +97,8 @@ def _fwd(**over):
     (dict(mbps=1 << 28), N.PKV_ERR_UNSUPPORTED),
     (dict(scale=float("inf")), N.PKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), N.PKV_ERR_INVALID_ARG),
+    (dict(scale=0.0), N.PKV_ERR_INVALID_ARG),
+    (dict(scale=-0.5), N.PKV_ERR_INVALID_ARG),
     (dict(q=0), N.PKV_ERR_INVALID_ARG),
     (dict(qsl=0), N.PKV_ERR_INVALID_ARG),
     (dict(out=FAKE + 4), N.PKV_ERR_INVALID_ARG),
@@ -130,7 +132,7 @@ def test_tuning_and_events_validation():
     lib = N.lib()
     assert lib.paged_attention_set_tuning(-1, 0, 0) == N.PKV_ERR_INVALID_ARG
     assert lib.paged_attention_set_tuning(0, 0, 3) == N.PKV_ERR_INVALID_ARG
-    assert lib.paged_attention_set_tuning(0, 0, 2) == N.PKV_ERR_INVALID_ARG
+    assert lib.paged_attention_set_tuning(0, 0, 2) == N.PKV_OK
     assert lib.paged_attention_set_tuning(0, 1 << 20, 0) == N.PKV_ERR_INVALID_ARG
     assert lib.paged_attention_set_tuning(0, 0, 0) == N.PKV_OK
     assert lib.paged_attention_set_profile_events(FAKE, None) == N.PKV_ERR_INVALID_ARG

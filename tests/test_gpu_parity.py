@@ -103,11 +103,32 @@ def test_item_counts(name, items):
     check_close(out_f64(out), outs[0], BF16, f"{name} items={items}")
 
 
+@pytest.mark.parametrize("kind", [1, 2])
+@pytest.mark.parametrize("partition", [0, 256])
+@pytest.mark.parametrize("name", ["decode", "mixed", "spec", "prefix"])
+def test_tile_kinds(name, partition, kind):
+    """Both row-tile shapes (16 or 32 rows per wave), with automatic or short partitions, give the
+    oracle's result."""
+    w = make_config(name, "small")
+    log(f"small {name} tile_kind={kind} partition={partition}")
+    pkv.set_tuning(partition, 0, kind)
+    dw = DeviceWorkload(w)
+    out = dw.run_step(0)
+    _, _, outs = _oracle_steps(w)
+    torch.cuda.synchronize()
+    check_close(out_f64(out), outs[0], BF16, f"{name} kind={kind} P={partition}")
+
+
+@pytest.mark.parametrize("kind", [1, 2])
 @pytest.mark.parametrize("dtype", [BF16, FP32])
 @pytest.mark.parametrize("head_dim,block_size,hq,hkv", [(64, 8, 8, 2), (64, 32, 4, 4), (128, 64, 16, 1),
                                                          (128, 256, 6, 3)])
-def test_geometries(dtype, head_dim, block_size, hq, hkv):
-    """head_dim 64/128, block sizes 8..256, MHA/GQA/MQA, ragged lengths including 1 and exact blocks."""
+def test_geometries(dtype, head_dim, block_size, hq, hkv, kind):
+    """head_dim 64/128, block sizes 8..256, MHA/GQA/MQA, ragged lengths including 1 and exact blocks,
+    under both row-tile shapes."""
+    if dtype == FP32 and kind == 2:
+        pytest.skip("the float32 path has no row tiles")
+    pkv.set_tuning(0, 0, kind)
     rng = np.random.default_rng(head_dim * 1000 + block_size + hq)
     q_lens = [1, 3, 1, 17, 0, 5, 1]
     ctx = [1, 3, block_size, 40 + 3 * block_size, 9, 2 * block_size + 1, 700]
@@ -130,7 +151,8 @@ def test_paging_invariance_and_determinism():
     out1 = dw.run_step(0).clone()
     st = dw.steps[0]
     out2 = pkv.paged_attention_forward(st["q"], dw.k_pool, dw.v_pool, dw.block_tables, st["context_lens"],
-                                       st["query_start_loc"], scale=w.scale)
+                                       st["query_start_loc"], scale=w.scale,
+                                       max_q_len=st["max_q_len"])
     # contiguous layout: sequence s occupies consecutive blocks
     L = w.steps[0].context_lens
     nblk = -(-L.astype(np.int64) // w.block_size)
@@ -146,7 +168,8 @@ def test_paging_invariance_and_determinism():
     kc = dw.k_pool[idx].contiguous()
     vc = dw.v_pool[idx].contiguous()
     out3 = pkv.paged_attention_forward(st["q"], kc, vc, to_torch(tables, None), st["context_lens"],
-                                       st["query_start_loc"], scale=w.scale)
+                                       st["query_start_loc"], scale=w.scale,
+                                       max_q_len=st["max_q_len"])
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
     assert torch.equal(out1, out3)
@@ -170,7 +193,8 @@ def test_garbage_invariance():
     vp[mask] = float("nan")
     st = dw.steps[0]
     out2 = pkv.paged_attention_forward(st["q"], kp, vp, dw.block_tables, st["context_lens"],
-                                       st["query_start_loc"], scale=w.scale)
+                                       st["query_start_loc"], scale=w.scale,
+                                       max_q_len=st["max_q_len"])
     torch.cuda.synchronize()
     assert torch.isfinite(out2.float()).all()
     assert torch.equal(out1, out2)
@@ -195,7 +219,8 @@ def test_shared_prefix_equals_private_copy():
     tables[0, :shared] = spare
     st = dw.steps[0]
     out2 = pkv.paged_attention_forward(st["q"], kp, vp, to_torch(tables, None), st["context_lens"],
-                                       st["query_start_loc"], scale=w.scale)
+                                       st["query_start_loc"], scale=w.scale,
+                                       max_q_len=st["max_q_len"])
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
 
@@ -216,7 +241,8 @@ def test_layer_inside_block_pool():
     st = dw.steps[0]
     pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], big_k[:, layer], big_v[:, layer])
     out = pkv.paged_attention_forward(st["q"], big_k[:, layer], big_v[:, layer], dw.block_tables,
-                                      st["context_lens"], st["query_start_loc"], scale=w.scale)
+                                      st["context_lens"], st["query_start_loc"], scale=w.scale,
+                                       max_q_len=st["max_q_len"])
     torch.cuda.synchronize()
     assert torch.equal(out, out_ref)
     assert torch.equal(big_k[:, layer], dw.k_pool)
