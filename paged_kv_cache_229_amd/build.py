@@ -23,7 +23,8 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["capi.cpp", "kv_write.hip", "attention_plan.hip", "attention_bf16.hip", "attention_fp32.hip"]
+SOURCES = ["capi.cpp", "kv_write.hip", "attention_plan.hip", "attention_bf16.hip", "attention_wide.hip",
+           "attention_fp32.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -37,10 +38,10 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The bf16 attention kernel compares raw MFMA scores with fmaxf; without NaN
+# Per-source extra flags.  The bf16 attention kernels compare raw MFMA scores with fmaxf; without NaN
 # semantics those become plain v_max3_f32 (no canonicalising copies).  NaN inputs give NaN or unspecified
 # output either way.
-EXTRA_FLAGS = {"attention_bf16.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"attention_bf16.hip": ["-fno-honor-nans"], "attention_wide.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

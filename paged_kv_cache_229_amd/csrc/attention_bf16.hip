@@ -33,68 +33,11 @@
 //    merges them.  Unsplit tiles write the normalised bf16 output directly.
 #include <type_traits>
 
+#include "device_util.h"
 #include "kernels.h"
 
 namespace pkv {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_AS __attribute__((address_space(3)))
-#define GLOBAL_AS __attribute__((address_space(1)))
-#define CONST_AS __attribute__((address_space(4)))
-
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// D[m][n] += sum_k A[m][k] B[k][n] over a 16x16x32 tile; lane l holds A[l%16][8(l/16) + 0..7],
-// B[8(l/16) + 0..7][l%16] and D[4(l/16) + 0..3][l%16].
-__device__ inline f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 16-byte HBM -> LDS copy per lane: lane l's 16 bytes from `src` land at LDS byte address
-// lds_base + 16*l (lds_base uniform).  Issued as inline assembly so that the compiler's wait-count pass
-// does not treat every later LDS read as dependent on it (it cannot tell ring slots apart and would drain
-// all loads in flight); readiness of a slot is established explicitly with wait_vmem + a barrier.
-// The copy is marked non-temporal: K/V are streamed once per (kv head, partition), and on MI355X the
-// streaming policy raises the sustained HBM read rate of this access pattern by about 12%.
-__device__ inline void dma16(const void* src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-               :
-               : "v"(src), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// s_waitcnt on the vector-memory counter only: at most N vector memory operations still outstanding.
-template <int N>
-__device__ inline void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Maximum over the four lanes l % 16 + 16 * {0, 1, 2, 3} (the lanes holding one row's scores): a swap of
-// the wave halves, then of neighbouring 16-lane rows, each followed by a max of the two copies.
-__device__ inline float row_max4(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// A row's reference maximum (log2 units) moves only when a chunk's maximum exceeds it by more than this,
-// so probabilities stay below 2^kLazyRescale and the accumulator is rescaled rarely; acc, l and m stay
-// mutually consistent, so the normalised result is unchanged.
-constexpr float kLazyRescale = 8.f;
-
-// 16-byte-chunk swizzle of LDS row `key`.
-template <int D>
-__device__ inline int k_swizzle(int key) {
-  return D == 128 ? (key & 15) : ((key >> 1) & 7);
-}
 
 template <int D, int NTW>
 struct Geo {
@@ -107,7 +50,7 @@ struct Geo {
   static constexpr int DT = D / 16;          // 16-channel output tiles
   static constexpr int WROWS = 16 * NTW;     // rows one wave owns
   static constexpr int RT = NW * WROWS;      // rows per tile
-  static_assert(RT == tile_rows_of(NTW), "the plan and the kernel agree on the tile height");
+  static_assert(NTW != 1 || RT == tile_rows_of(1), "the plan and the kernel agree on the tile height");
   static constexpr int ROWB = 2 * D;         // bytes of one key row in LDS
   static constexpr int TILEB = kStageKeys * ROWB;
   static constexpr int STAGEB = 2 * TILEB;   // K tile + V tile
@@ -480,9 +423,9 @@ attn_bf16_kernel(const AttnParams p) {
 }  // namespace
 
 int attention_bf16_wgs_per_cu(int head_dim, int tile_kind) {
+  if (tile_kind == 2) return attention_wide_wgs_per_cu(head_dim);
   // 160 KiB of LDS per CU; a workgroup holds the 4-stage K/V ring (reused for the merge) plus a word.
-  const int smem = tile_kind == 1 ? (head_dim == 128 ? Geo<128, 1>::SMEM : Geo<64, 1>::SMEM)
-                                  : (head_dim == 128 ? Geo<128, 2>::SMEM : Geo<64, 2>::SMEM);
+  const int smem = head_dim == 128 ? Geo<128, 1>::SMEM : Geo<64, 1>::SMEM;
   const int lds = smem + 64;
   int wgs = (160 * 1024) / lds;
   return wgs < 1 ? 1 : (wgs > 2 ? 2 : wgs);
@@ -490,14 +433,10 @@ int attention_bf16_wgs_per_cu(int head_dim, int tile_kind) {
 
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
                                  hipStream_t stream) {
+  if (tile_kind == 2) return launch_attention_wide(p, head_dim, grid, stream);
   const dim3 g(static_cast<unsigned>(grid)), b(kAttnThreads);
-  if (tile_kind == 1) {
-    if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), g, b, 0, stream, p);
-  } else {
-    if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), g, b, 0, stream, p);
-  }
+  if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);
+  else hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), g, b, 0, stream, p);
   return hipGetLastError();
 }
 

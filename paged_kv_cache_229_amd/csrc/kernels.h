@@ -10,12 +10,12 @@ namespace pkv {
 // of it.
 constexpr int kStageKeys = 64;
 constexpr int kThreads = 256;
-// The bf16 attention workgroup: 8 waves (two per SIMD).  Tile kind k: each wave owns k 16-row n-tiles,
-// so a tile has 128 (kind 1) or 256 (kind 2) rows.  Kind 1 suits rows-poor batches (decode, speculative
-// decode), kind 2 long query chunks, where each K/V fragment read from LDS then feeds two MFMAs.
+// Row-tile kinds of the bf16 attention.  Kind 1: 128-row tiles, 8 waves of 16 rows (two waves per SIMD),
+// for rows-poor batches (decode, speculative decode).  Kind 2: 256-row tiles, 4 waves of 64 rows (one
+// wave per SIMD, 32 x 32 MFMA tiles), for long query chunks.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int tile_rows_of(int kind) { return 16 * kind * kAttnWaves; }
+constexpr int tile_rows_of(int kind) { return kind == 1 ? 128 : 256; }
 constexpr int kMaxTileRows = tile_rows_of(2);
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
@@ -97,9 +97,11 @@ struct KvWriteParams {
 
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
-// grid = persistent workgroups; tile_kind is reserved (one tile shape today).
+// grid = persistent workgroups; tile_kind 1 runs the 16-row kernel, 2 the 64-row (wide) one.
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
                                  hipStream_t stream);
+hipError_t launch_attention_wide(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
+int attention_wide_wgs_per_cu(int head_dim);
 hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream);
 hipError_t launch_attention_fp32(const AttnParams& p, int head_dim, hipStream_t stream);
 // Workgroups per CU the bf16 attention kernel is built for (from its LDS footprint).
