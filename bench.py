@@ -196,6 +196,10 @@ def main() -> None:
           flush=True)
     work = algorithmic_work(w)
     traffic_key = w.name if args.subset == "all" else f"{w.name}:{args.subset}"
+    # The library runs the 16-row kernel when every sequence's rows (q_len x group) fit a 128-row tile and
+    # the 32x32 one otherwise (same rule as its automatic tile choice, given the q-length hint).
+    max_rows = int(np.diff(w.steps[0].query_start_loc).max()) * (w.num_q_heads // w.num_kv_heads)
+    kernel_name = "attn_bf16_kernel" if (args.tile_kind or (1 if max_rows <= 128 else 2)) == 1 else "attn_wide_kernel"
     st = w.steps[0]
 
     def t(a, is_data=True):
@@ -272,7 +276,7 @@ def main() -> None:
         "attention_logical_gbs": round(work["attn_bytes_logical"] / (k_avg * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(traffic_key),
-                     "kernel": "attn_bf16_kernel",
+                     "kernel": kernel_name,
                      "bytes_per_launch": work["attn_bytes_unique"]},
     }
     if args.subset == "prefill":

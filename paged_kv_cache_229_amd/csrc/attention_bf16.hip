@@ -8,6 +8,9 @@
 // (ADR 004 "Paged Attention Serving Integration", Consequences: prefill and decode share one call) and
 // grouped kv heads (the same comment: MQA/GQA) are handled by one kernel.
 //
+// This kernel serves row tiles of 128 rows (decode, speculative decode); long query chunks go to
+// attention_wide.hip, which runs the same pipeline on 32 x 32 MFMA tiles.
+//
 // How (gfx950 design, not a translation of any kernel the pages name):
 //  * Work item = (unit, kv head) from the device plan; a persistent grid pops items from a queue.  The
 //    rows of an item are (query token, head of g's group) pairs, so all G heads sharing kv head g read
