@@ -38,10 +38,12 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The bf16 attention kernels compare raw MFMA scores with fmaxf; without NaN
-# semantics those become plain v_max3_f32 (no canonicalising copies).  NaN inputs give NaN or unspecified
-# output either way.
-EXTRA_FLAGS = {"attention_bf16.hip": ["-fno-honor-nans"], "attention_wide.hip": ["-fno-honor-nans"]}
+# Per-source extra flags for the bf16 attention kernels.  They compare raw MFMA scores with fmaxf; without
+# NaN semantics those become plain v_max3_f32 (no canonicalising copies); NaN inputs give NaN or unspecified
+# output either way.  Their work-queue pops are single-lane atomics whose results are consumed after an
+# explicit wait; the atomic optimiser would turn each into a wave reduction that waits at once.
+_ATTN_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+EXTRA_FLAGS = {"attention_bf16.hip": _ATTN_FLAGS, "attention_wide.hip": _ATTN_FLAGS}
 
 
 def hipcc() -> str:

@@ -125,13 +125,15 @@ attn_bf16_kernel(const AttnParams p) {
     __syncthreads();
     if (item >= total_items) break;
 
+    // The plan's arrays are read-only here: scalar loads (constant address space) keep these reads off
+    // the vector-memory counter.
     const int unit = item / Hkv;
     const int g = item - unit * Hkv;
-    const int4 u = p.buf.units[unit];
-    const int s = u.x, tile = u.y, part = u.z, pbase = u.w;
-    const int q0 = p.query_start_loc[s];
-    const int n = p.query_start_loc[s + 1] - q0;
-    const int L = p.context_lens[s];
+    const CONST_AS int* const urec = (const CONST_AS int*)p.buf.units + 4 * unit;
+    const int s = urec[0], tile = urec[1], part = urec[2], pbase = urec[3];
+    const int q0 = ((const CONST_AS int*)p.query_start_loc)[s];
+    const int n = ((const CONST_AS int*)p.query_start_loc)[s + 1] - q0;
+    const int L = ((const CONST_AS int*)p.context_lens)[s];
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;
