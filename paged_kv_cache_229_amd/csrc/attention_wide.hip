@@ -20,6 +20,8 @@
 //  * Lazy online softmax as in the 16-row kernel (reference maximum moves only on growth beyond 2^8).
 //  * Tiles with few rows (decode-like units of a mixed batch) split the keys among the waves, whose states
 //    are merged through LDS; split partitions write (acc, m, l) for split_reduce_kernel.
+#include <type_traits>
+
 #include "device_util.h"
 #include "kernels.h"
 
@@ -157,8 +159,10 @@ attn_wide_kernel(const AttnParams p) {
       }
     };
     // Wave w copies keys [KPW*w, KPW*(w+1)) of stage st into ring slot st % NBUF; keys at or past ke are
-    // clamped to row ke-1 of the same block and masked.
-    auto issue = [&](int st, const int* phys) {
+    // clamped to row ke-1 of the same block and masked.  Row-split items (long chunks: the tiles of one
+    // sequence re-read its K/V) copy with the default cache policy, key-split ones stream non-temporally.
+    auto issue_p = [&](int st, const int* phys, auto keep_tag) __attribute__((always_inline)) {
+      constexpr bool KEEP = decltype(keep_tag)::value;
       unsigned char* const kdst = smem + (st & (T::NBUF - 1)) * T::STAGEB;
       const int key0 = kb + st * kStageKeys + T::KPW * wave;
 #pragma unroll
@@ -171,9 +175,18 @@ attn_wide_kernel(const AttnParams p) {
                           (static_cast<int64_t>(kk & bs_mask) * Hkv + g) * D + c * 8;
         const unsigned dk =
             lds_ring + static_cast<unsigned>((kdst - smem) + (T::KPW * wave + T::KPL * i) * T::ROWB);
-        dma16(kc + e, dk);
-        dma16(vc + e, dk + T::TILEB);
+        if (KEEP) {
+          dma16_keep(kc + e, dk);
+          dma16_keep(vc + e, dk + T::TILEB);
+        } else {
+          dma16(kc + e, dk);
+          dma16(vc + e, dk + T::TILEB);
+        }
       }
+    };
+    auto issue = [&](int st, const int* phys) __attribute__((always_inline)) {
+      if (WK == 1) issue_p(st, phys, std::true_type{});
+      else issue_p(st, phys, std::false_type{});
     };
 
     int tb0[T::NL], tb1[T::NL], tb2[T::NL], tbn[T::NL];

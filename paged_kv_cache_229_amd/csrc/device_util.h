@@ -46,6 +46,15 @@ __device__ inline void dma16(const void* src, unsigned lds_base) {
                : "memory", "m0");
 }
 
+// The same copy with the default cache policy, for K/V that several row tiles read close together (long
+// query chunks), so that L2 can serve the later reads.
+__device__ inline void dma16_keep(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // s_waitcnt on the vector-memory counter only: at most N vector memory operations still outstanding.
 template <int N>
 __device__ inline void wait_vmem() {
