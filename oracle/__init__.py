@@ -28,3 +28,4 @@ from .paged_kv import (  # noqa: F401
     softmax_rows,
     to_float64,
 )
+from .block_manager import BlockManagerOracle, CacheError, copy_blocks  # noqa: F401,E402
