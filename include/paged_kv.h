@@ -1,7 +1,7 @@
 /*
  * paged_kv.h — C ABI of the MI355X (gfx950) paged KV-cache library.
  *
- * Two operations, as the pages state the problem:
+ * Two operations, as the pages state the problem, and the cache manager they need:
  *
  *   paged_kv_write           scatter this step's new K/V rows into fixed-size physical blocks through a
  *                            slot mapping ("Paged Attention 基础 – 原理与实现进度", §3.2 status table:
@@ -14,6 +14,8 @@
  *                            model writes K/V into blocks, then reads through the paged call with the
  *                            per-layer slice k_cache[i]; Consequences: prefill and decode share one
  *                            multi-token call).
+ *   pkv_cm_* / paged_kv_copy_blocks  host cache manager (block allocator, block tables, slot mapping,
+ *                            shared blocks with copy on write) and its device block copy (declared below).
  *
  * Conventions shared by every entry point:
  *
@@ -54,7 +56,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes, misalignment */
   PKV_ERR_UNSUPPORTED = -2, /* outside the supported set above */
   PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than paged_attention_workspace_size() */
-  PKV_ERR_HIP = -4          /* a HIP launch or runtime call failed; message names it */
+  PKV_ERR_HIP = -4,         /* a HIP launch or runtime call failed; message names it */
+  PKV_ERR_NO_BLOCKS = -5    /* the cache manager has too few free blocks; nothing changed */
 } pkv_status;
 
 typedef enum { PKV_FP32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -127,6 +130,83 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                             int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
                             int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * paged_kv_copy_blocks — for i < num_pairs: block dst_blocks[i] of both caches takes the contents of
+ * block src_blocks[i] (this layer's block_size * num_kv_heads * head_dim elements, bit for bit).  The
+ * device half of copy on write: run it with the (src, dst) pair pkv_cm_append reports, before writing the
+ * new slots.  Pool geometry and checks as in paged_kv_write.
+ *
+ *   src_blocks, dst_blocks (device) [num_pairs] int32; ids outside [0, num_blocks) are skipped.  Pairs
+ *                 run concurrently: no dst may be another pair's src or dst (the manager's pairs never are).
+ *   num_pairs     0 is a no-op; at most 65535 (PKV_ERR_UNSUPPORTED above).
+ */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, int32_t block_size,
+                         int64_t block_stride, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs,
+                         void* stream);
+
+/*
+ * Cache manager (host memory and host calls only; no HIP call, no device pointer).  It owns the mapping
+ * from sequences to physical blocks: a block allocator, one block table per sequence id, the slot mapping
+ * of new tokens, and blocks shared by several sequences ("Paged Attention 基础", §1 problems 1-3 and
+ * §3.1 A: block allocator, block table, slot mapping; §2 figure: sequences A [7, 3] and B [7, 9] share
+ * block 7; ADR 004, Decision 5 and Consequences: one update call for fresh and growing sequences,
+ * free(seq_id), add_prefix / try_get_prefix_blocks).
+ *
+ *  - Allocation takes the lowest-numbered free block.  A block is shared by reference counting: each
+ *    sequence and each registered prefix listing it holds one reference; it is free again at zero.
+ *  - Every call either completes or changes nothing (PKV_ERR_NO_BLOCKS, PKV_ERR_INVALID_ARG).
+ *  - A manager is not thread-safe; it is owned by its creator and released with pkv_cm_destroy.
+ */
+typedef struct pkv_cache_manager pkv_cache_manager;
+
+/* A manager over num_blocks blocks of block_size tokens, all free.  NULL (last error set) on
+ * num_blocks < 1, block_size < 1, or num_blocks * block_size >= 2^31. */
+pkv_cache_manager* pkv_cm_create(int32_t num_blocks, int32_t block_size);
+void pkv_cm_destroy(pkv_cache_manager* manager);
+
+/* Free blocks; -1 for a NULL manager. */
+int32_t pkv_cm_num_free(const pkv_cache_manager* manager);
+
+/* Tokens held by seq_id; -1 if unknown. */
+int32_t pkv_cm_seq_len(const pkv_cache_manager* manager, int64_t seq_id);
+
+/*
+ * Append num_tokens tokens at the end of seq_id (created if new): the update call of a prefill or decode
+ * step.  Takes the blocks the new length needs; slots_out (host, [num_tokens]) receives the pool row of
+ * each new position in order (block_table[pos / block_size] * block_size + pos % block_size), ready for
+ * paged_kv_write.  If the last block is partly filled and shared, it is first replaced by a fresh copy:
+ * cow_out (host, [2]) receives (src, dst) — copy block src to dst with paged_kv_copy_blocks before
+ * writing — else (-1, -1).  PKV_ERR_NO_BLOCKS when the free blocks do not suffice.
+ */
+int pkv_cm_append(pkv_cache_manager* manager, int64_t seq_id, int32_t num_tokens, int32_t* slots_out,
+                  int32_t* cow_out);
+
+/* Release seq_id: each of its blocks loses one reference. */
+int pkv_cm_free(pkv_cache_manager* manager, int64_t seq_id);
+
+/* child (new) starts as parent's copy, sharing every block (one more reference each). */
+int pkv_cm_fork(pkv_cache_manager* manager, int64_t parent, int64_t child);
+
+/* Register the blocks holding the first num_tokens tokens of seq_id (1 <= num_tokens <= its length)
+ * under key; the registry keeps one reference, so they outlive the sequence.  The key must be new. */
+int pkv_cm_add_prefix(pkv_cache_manager* manager, uint64_t key, int64_t seq_id, int32_t num_tokens);
+
+/* A new seq_id starts with the prefix registered under key (shared blocks); *tokens_out = its length,
+ * or 0 (and nothing created) when the key is unknown. */
+int pkv_cm_attach_prefix(pkv_cache_manager* manager, uint64_t key, int64_t seq_id, int32_t* tokens_out);
+
+/* Release the registry's references of key. */
+int pkv_cm_drop_prefix(pkv_cache_manager* manager, uint64_t key);
+
+/*
+ * Per-step metadata for a batch: block_tables_out (host, [num_seqs][max_blocks_per_seq], row-major)
+ * receives each sequence's blocks padded with -1, context_lens_out (host, [num_seqs]) its length.
+ * Fails, writing nothing, if a sequence is unknown or holds more than max_blocks_per_seq blocks.
+ */
+int pkv_cm_build_tables(const pkv_cache_manager* manager, const int64_t* seq_ids, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, int32_t* block_tables_out, int32_t* context_lens_out);
 
 /*
  * Tuning and measurement (per calling thread; they change how work is divided, never the result beyond

@@ -7,6 +7,8 @@ the library's kernels.  PyTorch supplies device memory and streams.
     paged_kv_write(k, v, slot_mapping, k_cache, v_cache)
     out = paged_attention_forward(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
                                   scale=None)
+    mgr = CacheManager(num_blocks, block_size)        # host block allocator, tables, slot mapping
+    slots, cow = mgr.append(seq_id, num_tokens)       # cow: (src, dst) block to copy_blocks() first
 
 The two calls follow the problem as the pages state it: new K/V rows go through a slot mapping into
 fixed-size physical blocks, and attention reads each sequence's K/V through its block table, with
@@ -43,6 +45,8 @@ __all__ = [
     "set_profile_events",
     "validate_metadata",
     "PagedKVError",
+    "CacheManager",
+    "copy_blocks",
 ]
 
 _DTYPES = {torch.bfloat16: PKV_BF16, torch.float32: PKV_FP32}
@@ -204,3 +208,6 @@ def validate_metadata(*, block_tables=None, context_lens=None, query_start_loc=N
             row = bt[s, :nblk[s]]
             if np.any(row < 0) or np.any(row >= num_blocks):
                 raise ValueError(f"sequence {s} names a block outside the pool")
+
+
+from .cache_manager import CacheManager, copy_blocks  # noqa: E402  (uses the helpers above)

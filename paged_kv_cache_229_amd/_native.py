@@ -19,6 +19,7 @@ PKV_ERR_INVALID_ARG = -1
 PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
+PKV_ERR_NO_BLOCKS = -5
 PKV_FP32 = 0
 PKV_BF16 = 1
 
@@ -28,11 +29,13 @@ STATUS_NAMES = {
     PKV_ERR_UNSUPPORTED: "PKV_ERR_UNSUPPORTED",
     PKV_ERR_WORKSPACE: "PKV_ERR_WORKSPACE",
     PKV_ERR_HIP: "PKV_ERR_HIP",
+    PKV_ERR_NO_BLOCKS: "PKV_ERR_NO_BLOCKS",
 }
 
 # Every symbol include/paged_kv.h declares, with its ctypes signature.
 _c = ctypes
 _vp, _i32, _i64, _sz, _f32 = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_size_t, _c.c_float
+_u64 = _c.c_uint64
 SIGNATURES = {
     "paged_kv_abi_version": (_c.c_int, []),
     "paged_kv_last_error": (_c.c_char_p, []),
@@ -43,6 +46,18 @@ SIGNATURES = {
                                            _vp]),
     "paged_attention_set_tuning": (_c.c_int, [_i32, _i32, _i32]),
     "paged_attention_set_profile_events": (_c.c_int, [_vp, _vp]),
+    "paged_kv_copy_blocks": (_c.c_int, [_vp, _vp, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "pkv_cm_create": (_vp, [_i32, _i32]),
+    "pkv_cm_destroy": (None, [_vp]),
+    "pkv_cm_num_free": (_i32, [_vp]),
+    "pkv_cm_seq_len": (_i32, [_vp, _i64]),
+    "pkv_cm_append": (_c.c_int, [_vp, _i64, _i32, _vp, _vp]),
+    "pkv_cm_free": (_c.c_int, [_vp, _i64]),
+    "pkv_cm_fork": (_c.c_int, [_vp, _i64, _i64]),
+    "pkv_cm_add_prefix": (_c.c_int, [_vp, _u64, _i64, _i32]),
+    "pkv_cm_attach_prefix": (_c.c_int, [_vp, _u64, _i64, _vp]),
+    "pkv_cm_drop_prefix": (_c.c_int, [_vp, _u64]),
+    "pkv_cm_build_tables": (_c.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
 }
 
 _LIB = None

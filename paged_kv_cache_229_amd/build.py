@@ -23,8 +23,8 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["capi.cpp", "kv_write.hip", "attention_plan.hip", "attention_bf16.hip", "attention_wide.hip",
-           "attention_fp32.hip"]
+SOURCES = ["capi.cpp", "cache_manager.cpp", "kv_write.hip", "copy_blocks.hip", "attention_plan.hip",
+           "attention_bf16.hip", "attention_wide.hip", "attention_fp32.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 thread_local std::string g_error;
 thread_local int g_partition_keys = 0;
@@ -34,6 +34,16 @@ int succeed() {
 }
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+}  // namespace
+
+// The status protocol for the library's other host sources (the cache manager).
+namespace pkv {
+int host_fail(int status, const std::string& msg) { return fail(status, msg); }
+int host_ok() { return succeed(); }
+}  // namespace pkv
+
+namespace {
 
 int log2i(int64_t x) {
   int r = 0;
@@ -171,6 +181,33 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
   p.block_stride_bytes = stride * elem_bytes(dtype);
   const hipError_t e = pkv::launch_kv_write(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("paged_kv_write launch", e);
+  return succeed();
+}
+
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, int32_t block_size,
+                         int64_t block_stride, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs,
+                         void* stream) {
+  int64_t stride = 0;
+  const int st = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs must be >= 0");
+  if (num_pairs == 0) return succeed();
+  if (num_pairs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 pairs per call");
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PKV_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+  pkv::CopyBlocksParams p{};
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.src = src_blocks;
+  p.dst = dst_blocks;
+  p.num_blocks = num_blocks;
+  p.chunks_per_block = static_cast<int64_t>(block_size) * num_kv_heads * head_dim * elem_bytes(dtype) / 16;
+  p.block_stride_bytes = stride * elem_bytes(dtype);
+  const hipError_t e = pkv::launch_copy_blocks(p, num_pairs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, std::string("copy_blocks launch: ") + hipGetErrorString(e));
   return succeed();
 }
 

@@ -95,7 +95,18 @@ struct KvWriteParams {
   int64_t block_stride_bytes;
 };
 
+struct CopyBlocksParams {
+  void* k_cache;
+  void* v_cache;
+  const int* src;
+  const int* dst;
+  int64_t num_blocks;
+  int64_t chunks_per_block;    // 16-byte chunks of one block of this layer
+  int64_t block_stride_bytes;
+};
+
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, int num_pairs, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 // grid = persistent workgroups; tile_kind 1 runs the 16-row kernel, 2 the 64-row (wide) one.
 hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
         assert name in N.SIGNATURES, f"{name} declared in the header but not bound"
         assert hasattr(lib, name), f"{name} not exported"
     assert set(N.SIGNATURES) == set(names)
-    assert lib.paged_kv_abi_version() == 1
+    assert lib.paged_kv_abi_version() == 2
 
 
 def test_single_hip_runtime_loaded():
@@ -115,6 +115,32 @@ def test_forward_rejects(over, status):
 def test_forward_empty_is_noop():
     assert _fwd(N=0, out=0, q=0, kc=0, vc=0, bt=0, ctx=0, qsl=0) == N.PKV_OK
     assert _fwd(T=0, out=0, q=0) == N.PKV_OK
+
+
+def _copy(**over):
+    a = dict(kc=FAKE, vc=FAKE, nb=16, bs=16, stride=0, hkv=2, d=64, dtype=N.PKV_BF16, src=FAKE, dst=FAKE, n=3)
+    a.update(over)
+    return N.lib().paged_kv_copy_blocks(a["kc"], a["vc"], a["nb"], a["bs"], a["stride"], a["hkv"], a["d"],
+                                        a["dtype"], a["src"], a["dst"], a["n"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n=-1), N.PKV_ERR_INVALID_ARG),
+    (dict(n=70000), N.PKV_ERR_UNSUPPORTED),
+    (dict(src=0), N.PKV_ERR_INVALID_ARG),
+    (dict(kc=0), N.PKV_ERR_INVALID_ARG),
+    (dict(vc=FAKE + 8), N.PKV_ERR_INVALID_ARG),
+    (dict(d=96), N.PKV_ERR_UNSUPPORTED),
+    (dict(bs=12), N.PKV_ERR_UNSUPPORTED),
+    (dict(nb=0), N.PKV_ERR_INVALID_ARG),
+])
+def test_copy_blocks_rejects(over, status):
+    assert _copy(**over) == status
+    assert N.lib().paged_kv_last_error()
+
+
+def test_copy_blocks_empty_is_noop():
+    assert _copy(n=0, src=0, dst=0, kc=0, vc=0) == N.PKV_OK
 
 
 def test_workspace_size():
