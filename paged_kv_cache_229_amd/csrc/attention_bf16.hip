@@ -82,6 +82,7 @@ attn_bf16_kernel(const AttnParams p) {
   const int Hq = p.num_q_heads;
   const int total_items = p.buf.hdr[kHdrUnits] * Hkv;
   const int P = p.buf.hdr[kHdrPartition];
+  const int Pw = p.buf.hdr[kHdrPartitionWide];
   const int bs_log2 = p.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int last_block = static_cast<int>(p.num_blocks - 1);
@@ -130,15 +131,14 @@ attn_bf16_kernel(const AttnParams p) {
     const int unit = item / Hkv;
     const int g = item - unit * Hkv;
     const CONST_AS int* const urec = (const CONST_AS int*)p.buf.units + 4 * unit;
-    const int s = urec[0], tile = urec[1], part = urec[2], pbase = urec[3];
+    const int s = urec[0], tile = urec[1], kb = urec[2], pbase = urec[3];
     const int q0 = ((const CONST_AS int*)p.query_start_loc)[s];
     const int n = ((const CONST_AS int*)p.query_start_loc)[s + 1] - q0;
     const int L = ((const CONST_AS int*)p.context_lens)[s];
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;
-    const int kb = part * P;
-    const int ke = min(kmax, kb + P);
+    const int ke = min(kmax, kb + (rows_here > kSmallTileRows ? Pw : P));
     const int WR = rows_here <= T::WROWS ? 1
                    : rows_here <= 2 * T::WROWS ? 2
                    : rows_here <= 4 * T::WROWS ? 4 : 8;

@@ -1,16 +1,18 @@
 // Device-side work plan and split-context reduction for paged attention.
 //
 // The host never reads context_lens or query_start_loc (that would need a device-to-host sync), so the
-// decomposition into work is made here, on the device, in one small workgroup:
+// decomposition into work is made here, on the device, by one wave:
 //
 //   unit = (sequence s, row tile t, context partition p), processed once per kv head.
 //
 // The rows of (s, kv head g) are the pairs (query token i, query head of g's group), row = i * G + h',
 // so a tile holds several tokens' worth of grouped heads and the keys it loads serve all of them.  Row
 // tile t covers rows [t*RT, min(rows, (t+1)*RT)); its last token sees keys [0, kmax).  A tile whose kmax
-// exceeds the partition length P is split into ceil(kmax / P) partitions; P is picked so the whole call
-// has about `target_items` (unit, kv head) items, enough to fill 256 compute units several times over,
-// and then lengthened until the split tiles' partial rows fit the workspace.  Units are listed longest
+// exceeds its partition length is split into ceil(kmax / length) partitions.  Tiles of at most
+// kSmallTileRows rows (decode-like work) use P, picked so the whole call has about `target_items`
+// (unit, kv head) items, enough to fill 256 compute units several times over; taller tiles (long query
+// chunks) use max(P, kWidePartitionMin).  P is then lengthened until the split tiles' partial rows fit
+// the workspace.  Units are listed longest
 // first (counting sort on their 64-key stage count) so that the attention kernel's static, snake-ordered
 // assignment of items to workgroups stays balanced.
 //
@@ -25,20 +27,53 @@
 namespace pkv {
 namespace {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
+// One wave plans the whole call: every step is a per-lane loop over sequences s = lane, lane + 64, ...
+// followed by wave reductions or scans, so the kernel needs no workgroup barrier.  Each sequence's
+// (new tokens, context, tiles) is read from global memory once and kept in LDS (for the first
+// kSeqCache sequences; later ones are read again), and all arithmetic is 32-bit: 64-bit division is a
+// long software routine on this GPU.
+constexpr int kPlanLanes = 64;
 constexpr int kSortBuckets = 1024;
+constexpr int kBucketsPerLane = kSortBuckets / kPlanLanes;
+constexpr int kSeqCache = 2048;
 
 __device__ inline bool seq_ok(int q_lo, int q_hi, int context_len, int64_t total_q, int max_context) {
   return q_lo >= 0 && q_hi >= q_lo && q_hi <= total_q && context_len >= q_hi - q_lo &&
          context_len <= max_context;
 }
 
-// One past the last key the tile's last row may see.
-__device__ inline int tile_kmax(int context_len, int n, int group, int rows, int rows_per_tile, int t) {
-  const int last_row = min(rows, (t + 1) * rows_per_tile) - 1;
-  return context_len - n + last_row / group + 1;
-}
+// One past the last key tile t's last row may see (rows are token * G + head, so the row's token is
+// row / G).  When G divides the tile height every tile but the last ends on a token boundary and no
+// division is needed; the last tile's last row is the last token, which sees all L keys.
+struct TileGeom {
+  int G, RT, tokens_per_tile;  // tokens_per_tile = RT / G when G divides RT, else 0
+  __device__ int kmax(int L, int n, int rows, int t) const {
+    const int end = (t + 1) * RT;
+    if (end >= rows) return L;
+    if (tokens_per_tile > 0) return L - n + (t + 1) * tokens_per_tile;
+    return L - n + (end - 1) / G + 1;
+  }
+};
+
+// Division by a divisor fixed for many calls (2 <= d < 2^31): q = mulhi(n, m) with m = floor((2^32 - 1)
+// / d) + 1 is floor(n / d) or one more, since n m / 2^32 lies in [n / d, n / d + 1); one compare fixes it.
+struct FastDiv {
+  unsigned d, m;
+  __device__ explicit FastDiv(int divisor)
+      : d(static_cast<unsigned>(divisor)), m(0xffffffffu / static_cast<unsigned>(divisor) + 1u) {}
+  __device__ int floor_div(int n) const {
+    unsigned q = __umulhi(static_cast<unsigned>(n), m);
+    q -= q * d > static_cast<unsigned>(n) ? 1u : 0u;
+    return static_cast<int>(q);
+  }
+  // ceil(n / d) for 0 <= n < 2^31.
+  __device__ int ceil_div(int n) const {
+    const unsigned a = static_cast<unsigned>(n) + d - 1u;
+    unsigned q = __umulhi(a, m);
+    q -= q * d > a ? 1u : 0u;
+    return static_cast<int>(q);
+  }
+};
 
 // Stage-count bucket of a unit, longest first.
 __device__ inline int sort_bucket(int keys) {
@@ -46,63 +81,89 @@ __device__ inline int sort_bucket(int keys) {
   return kSortBuckets - 1 - min(stages, kSortBuckets - 1);
 }
 
-// Exclusive prefix sum over the workgroup (wave scans, then a scan of the wave totals);
-// *total receives the sum of all values.  `sm` holds kPlanWaves + 1 entries.
-__device__ long long block_exclusive_scan(long long v, long long* total, long long* sm) {
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  long long incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long x = __shfl_up(incl, off);
-    if (lane >= off) incl += x;
-  }
-  if (lane == 63) sm[wave] = incl;
-  __syncthreads();
-  if (t == 0) {
-    long long run = 0;
-    for (int w = 0; w < kPlanWaves; ++w) {
-      const long long x = sm[w];
-      sm[w] = run;
-      run += x;
-    }
-    sm[kPlanWaves] = run;
-  }
-  __syncthreads();
-  const long long excl = sm[wave] + incl - v;
-  *total = sm[kPlanWaves];
-  __syncthreads();
-  return excl;
+// Wave-wide inclusive prefix sum with DPP lane moves (no LDS traffic): running sums within each row of 16
+// lanes by shifts of 1, 2, 4 and 8, then row 0's total into row 1 and row 2's into row 3 (row_bcast:15),
+// then lane 31's running sum into rows 2 and 3 (row_bcast:31).  Lanes whose source is outside the row or
+// masked off add 0.
+__device__ inline int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
 }
 
-__device__ long long block_max(long long v, long long* sm) {
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<long long>(__shfl_xor(v, off)));
-  if (lane == 0) sm[wave] = v;
-  __syncthreads();
-  long long r = sm[0];
-  for (int w = 1; w < kPlanWaves; ++w) r = max(r, sm[w]);
-  __syncthreads();
-  return r;
+// Exclusive prefix sum over the lanes; *total receives the sum of all lanes.
+__device__ inline int wave_exclusive_scan(int v, int* total) {
+  const int incl = wave_inclusive_scan(v);
+  *total = __builtin_amdgcn_readlane(incl, 63);
+  return incl - v;
 }
 
-__global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) {
-  __shared__ long long sm[kPlanWaves + 1];
+__device__ inline int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_inclusive_scan(v), 63); }
+
+__device__ inline int wave_max(int v) {
+  // Values are >= 0, so lanes without a source may contribute 0.
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
   __shared__ int bucket[kSortBuckets];
-  const int t = threadIdx.x;
+  __shared__ int4 seqc[kSeqCache];  // (n, L, tiles, first partial row) per sequence
+  __shared__ int tbase[kSeqCache];  // first tile record per sequence
+  const int lane = threadIdx.x;
   const int N = p.num_seqs;
-  const int per = (N + kPlanThreads - 1) / kPlanThreads;
-  const int s0 = min(N, t * per);
-  const int s1 = min(N, s0 + per);
   const int RT = p.rows_per_tile;
   const int G = p.group;
-  const int* qsl = p.query_start_loc;
+  const int Hkv = p.num_kv_heads;
+  const int* const qsl = p.query_start_loc;
+  const int* const ctx = p.context_lens;
+  const TileGeom geo{G, RT, RT % G == 0 ? RT / G : 0};
+  // Per-lane partial counts only ever meet caps below 2^17; saturating them keeps every wave sum in
+  // 32 bits.
+  constexpr int kSat = 1 << 24;
 
-  long long work = 0, tiles = 0, bad = 0, maxk = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int lo = qsl[s], hi = qsl[s + 1], L = p.context_lens[s];
+  // (n, L, tiles) of sequence s; tiles is 0 for empty or invalid sequences.
+  auto seq = [&](int s, int& n, int& L) -> int {
+    if (s < kSeqCache) {
+      const int4 c = seqc[s];
+      n = c.x;
+      L = c.y;
+      return c.z;
+    }
+    const int lo = qsl[s];
+    n = qsl[s + 1] - lo;
+    L = ctx[s];
+    return p.buf.seq_tiles[s];
+  };
+
+  // Stage (first query, one past the last query, context) of the cached sequences in LDS; unrolled so
+  // that many loads are in flight at once.
+#pragma unroll 8
+  for (int s = lane; s < min(N, kSeqCache); s += kPlanLanes) seqc[s] = make_int4(qsl[s], qsl[s + 1], ctx[s], 0);
+
+  // Tiles per sequence, key work (in 64-key stages), longest context.
+  int work = 0, bad = 0, maxk = 0;
+  for (int s = lane; s < N; s += kPlanLanes) {
+    int lo, hi, L;
+    if (s < kSeqCache) {
+      const int4 c = seqc[s];
+      lo = c.x;
+      hi = c.y;
+      L = c.z;
+    } else {
+      lo = qsl[s];
+      hi = qsl[s + 1];
+      L = ctx[s];
+    }
     const int n = hi - lo;
     int nt = 0;
     if (!seq_ok(lo, hi, L, p.total_q, p.max_context)) {
@@ -110,120 +171,175 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const PlanParams p) 
     } else if (n > 0) {
       const int rows = n * G;
       nt = (rows + RT - 1) / RT;
-      for (int tt = 0; tt < nt; ++tt) {
-        const int km = tile_kmax(L, n, G, rows, RT, tt);
-        work += km;
-        maxk = max(maxk, static_cast<long long>(km));
-      }
+      for (int t = 0; t < nt; ++t) work = min(work + (geo.kmax(L, n, rows, t) + kStageKeys - 1) / kStageKeys, kSat);
+      maxk = max(maxk, L);  // the last tile's last row sees all L keys
     }
-    p.buf.seq_tiles[s] = nt;
-    tiles += nt;
+    if (s < kSeqCache) seqc[s] = make_int4(n, L, nt, 0);
+    else p.buf.seq_tiles[s] = nt;
   }
-  long long total_work, total_tiles, total_bad;
-  block_exclusive_scan(work, &total_work, sm);
-  block_exclusive_scan(bad, &total_bad, sm);
-  const long long tile_off = block_exclusive_scan(tiles, &total_tiles, sm);
-  const long long max_kmax = block_max(maxk, sm);
+  const long long total_work = static_cast<long long>(wave_sum(work)) * kStageKeys;
+  const int total_bad = wave_sum(bad);
+  const int max_kmax = wave_max(maxk);
+
+  // First tile record of every sequence, in sequence order.
+  int total_tiles = 0;
+  for (int base = 0; base < N; base += kPlanLanes) {
+    const int s = base + lane;
+    int n, L;
+    const int nt = s < N ? seq(s, n, L) : 0;
+    int sum;
+    const int first = total_tiles + wave_exclusive_scan(nt, &sum);
+    if (s < kSeqCache) tbase[s] = first;
+    if (s < N) p.buf.tile_base[s] = first;
+    total_tiles += sum;
+    if (total_tiles > p.tile_cap) break;
+  }
 
   if (total_tiles > p.tile_cap) {  // inconsistent metadata: do nothing
-    if (t == 0) {
+    if (lane == 0) {
       p.buf.hdr[kHdrUnits] = 0;
       p.buf.hdr[kHdrQueue] = 0;
       p.buf.hdr[kHdrPartition] = kStageKeys;
+      p.buf.hdr[kHdrPartitionWide] = kStageKeys;
       p.buf.hdr[kHdrTiles] = 0;
       p.buf.hdr[kHdrBadSeqs] = -1;
     }
     return;
   }
 
-  long long P;
+  // Partition length of small tiles: about target_items items in all, a multiple of the stage, at least
+  // kMinPartition, and never longer than needed for the longest context.  Taller tiles use Pw >= P.
+  const int pmax = max(kMinPartition, (max_kmax + kStageKeys - 1) / kStageKeys * kStageKeys);
+  int P;
   if (p.forced_partition > 0) {
-    P = (p.forced_partition + kStageKeys - 1) / kStageKeys * kStageKeys;
+    P = min((p.forced_partition + kStageKeys - 1) / kStageKeys * kStageKeys, pmax);
   } else {
-    const long long items = total_work * p.num_kv_heads;
+    const long long items = total_work * Hkv;
     const long long want = (items + p.target_items - 1) / p.target_items;
-    P = (want + kStageKeys - 1) / kStageKeys * kStageKeys;
-    if (P < kMinPartition) P = kMinPartition;
+    P = static_cast<int>(min(static_cast<long long>(pmax), (want + kStageKeys - 1) / kStageKeys * kStageKeys));
+    P = max(P, kMinPartition);
   }
+  auto wide_len = [&](int P_) { return p.forced_partition > 0 ? P_ : min(max(P_, kWidePartitionMin), pmax); };
 
-  // Partitions per tile and partial rows per split tile, for partition length P.
-  long long units_total = 0, prows_total = 0, prow_off = 0;
+  // Lengthen P until the units and the split tiles' partial rows fit the workspace.
+  int units_total = 0;
   for (;;) {
-    long long units = 0, prows = 0;
-    for (int s = s0; s < s1; ++s) {
-      const int nt = p.buf.seq_tiles[s];
-      if (nt == 0) continue;
-      const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
+    const int Pw = wide_len(P);
+    const FastDiv divp(P), divw(Pw);
+    int units = 0, prows = 0;
+    for (int s = lane; s < N; s += kPlanLanes) {
+      int n, L;
+      const int nt = seq(s, n, L);
       const int rows = n * G;
-      for (int tt = 0; tt < nt; ++tt) {
-        const long long np = (tile_kmax(L, n, G, rows, RT, tt) + P - 1) / P;
-        units += np;
-        if (np > 1) prows += np * min(RT, rows - tt * RT) * p.num_kv_heads;
+      for (int t = 0; t < nt; ++t) {
+        const int rows_t = min(RT, rows - t * RT);
+        const int km = geo.kmax(L, n, rows, t);
+        const int np = rows_t > kSmallTileRows ? divw.ceil_div(km) : divp.ceil_div(km);
+        units = min(units + np, kSat);
+        if (np > 1) prows = min(prows + min(np * rows_t, kSat) * Hkv, kSat);
       }
     }
-    block_exclusive_scan(units, &units_total, sm);
-    prow_off = block_exclusive_scan(prows, &prows_total, sm);
+    units_total = wave_sum(units);
+    const int prows_total = wave_sum(prows);
     if ((units_total <= p.unit_cap && prows_total <= p.prow_cap) || P >= max_kmax) break;
-    P *= 2;
+    P = P > pmax / 2 ? pmax : 2 * P;
+  }
+
+  const int Pw = wide_len(P);
+  const FastDiv divp(P), divw(Pw);
+  // Partition length and count of tile t of a sequence.
+  auto split = [&](int rows_t, int km, int& len) {
+    len = rows_t > kSmallTileRows ? Pw : P;
+    return rows_t > kSmallTileRows ? divw.ceil_div(km) : divp.ceil_div(km);
+  };
+  // First partial row of every sequence's split tiles, in sequence order.
+  {
+    int run = 0;
+    for (int base = 0; base < N; base += kPlanLanes) {
+      const int s = base + lane;
+      int pr = 0;
+      if (s < N) {
+        int n, L;
+        const int nt = seq(s, n, L);
+        const int rows = n * G;
+        for (int t = 0; t < nt; ++t) {
+          const int rows_t = min(RT, rows - t * RT);
+          int len;
+          const int np = split(rows_t, geo.kmax(L, n, rows, t), len);
+          if (np > 1) pr += np * rows_t * Hkv;
+        }
+      }
+      int sum;
+      const int first = run + wave_exclusive_scan(pr, &sum);
+      if (s < kSeqCache) seqc[s].w = first;
+      else if (s < N) p.buf.seq_units[s] = first;
+      run += sum;
+    }
   }
 
   // Counting sort of the units by stage count, longest first: histogram, bucket offsets, scatter.
-  for (int i = t; i < kSortBuckets; i += kPlanThreads) bucket[i] = 0;
+#pragma unroll
+  for (int i = 0; i < kBucketsPerLane; ++i) bucket[lane * kBucketsPerLane + i] = 0;
   __syncthreads();
-  for (int s = s0; s < s1; ++s) {
-    const int nt = p.buf.seq_tiles[s];
-    if (nt == 0) continue;
-    const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
+  for (int s = lane; s < N; s += kPlanLanes) {
+    int n, L;
+    const int nt = seq(s, n, L);
     const int rows = n * G;
-    for (int tt = 0; tt < nt; ++tt) {
-      const int km = tile_kmax(L, n, G, rows, RT, tt);
-      const int np = static_cast<int>((km + P - 1) / P);
-      for (int pp = 0; pp < np; ++pp) {
-        const int keys = static_cast<int>(min(static_cast<long long>(km) - pp * P, P));
-        atomicAdd(&bucket[sort_bucket(keys)], 1);
-      }
+    for (int t = 0; t < nt; ++t) {
+      const int km = geo.kmax(L, n, rows, t);
+      const int len = min(RT, rows - t * RT) > kSmallTileRows ? Pw : P;
+      for (int k0 = 0; k0 < km; k0 += len) atomicAdd(&bucket[sort_bucket(min(km - k0, len))], 1);
     }
   }
   __syncthreads();
   {
-    const long long c = t < kSortBuckets ? bucket[t] : 0;
-    long long dummy;
-    const long long off = block_exclusive_scan(c, &dummy, sm);
-    if (t < kSortBuckets) bucket[t] = static_cast<int>(off);
+    int c[kBucketsPerLane];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < kBucketsPerLane; ++i) {
+      c[i] = bucket[lane * kBucketsPerLane + i];
+      mine += c[i];
+    }
+    int dummy;
+    int off = wave_exclusive_scan(mine, &dummy);
+#pragma unroll
+    for (int i = 0; i < kBucketsPerLane; ++i) {
+      bucket[lane * kBucketsPerLane + i] = off;
+      off += c[i];
+    }
   }
   __syncthreads();
 
-  long long tb = tile_off, pr = prow_off;
-  for (int s = s0; s < s1; ++s) {
-    p.buf.tile_base[s] = static_cast<int>(tb);
-    const int nt = p.buf.seq_tiles[s];
+  for (int s = lane; s < N; s += kPlanLanes) {
+    int n, L;
+    const int nt = seq(s, n, L);
     if (nt == 0) continue;
-    const int lo = qsl[s], n = qsl[s + 1] - lo, L = p.context_lens[s];
     const int rows = n * G;
-    for (int tt = 0; tt < nt; ++tt) {
-      const int km = tile_kmax(L, n, G, rows, RT, tt);
-      const int np = static_cast<int>((km + P - 1) / P);
-      const int rows_t = min(RT, rows - tt * RT);
-      const int pb0 = np > 1 ? static_cast<int>(pr) : -1;
-      p.buf.tile_rec[tb] = make_int4(s, tt, pb0, np);
+    int tb = s < kSeqCache ? tbase[s] : p.buf.tile_base[s];
+    int pr = s < kSeqCache ? seqc[s].w : p.buf.seq_units[s];
+    for (int t = 0; t < nt; ++t) {
+      const int km = geo.kmax(L, n, rows, t);
+      const int rows_t = min(RT, rows - t * RT);
+      int len;
+      const int np = split(rows_t, km, len);
+      p.buf.tile_rec[tb] = make_int4(s, t, np > 1 ? pr : -1, np);
       ++tb;
       for (int pp = 0; pp < np; ++pp) {
-        const int keys = static_cast<int>(min(static_cast<long long>(km) - pp * P, P));
-        const int slot = atomicAdd(&bucket[sort_bucket(keys)], 1);
-        const int pb = np > 1 ? static_cast<int>(pr + static_cast<long long>(pp) * rows_t * p.num_kv_heads)
-                              : -1;
-        p.buf.units[slot] = make_int4(s, tt, pp, pb);
+        const int k0 = pp * len;
+        const int slot = atomicAdd(&bucket[sort_bucket(min(km - k0, len))], 1);
+        p.buf.units[slot] = make_int4(s, t, k0, np > 1 ? pr + pp * rows_t * Hkv : -1);
       }
-      if (np > 1) pr += static_cast<long long>(np) * rows_t * p.num_kv_heads;
+      if (np > 1) pr += np * rows_t * Hkv;
     }
   }
-  if (t == 0) {
-    p.buf.tile_base[N] = static_cast<int>(total_tiles);
-    p.buf.hdr[kHdrUnits] = static_cast<int>(units_total);
+  if (lane == 0) {
+    p.buf.tile_base[N] = total_tiles;
+    p.buf.hdr[kHdrUnits] = units_total;
     p.buf.hdr[kHdrQueue] = 0;
-    p.buf.hdr[kHdrPartition] = static_cast<int>(P);
-    p.buf.hdr[kHdrTiles] = static_cast<int>(total_tiles);
-    p.buf.hdr[kHdrBadSeqs] = static_cast<int>(total_bad);
+    p.buf.hdr[kHdrPartition] = P;
+    p.buf.hdr[kHdrPartitionWide] = Pw;
+    p.buf.hdr[kHdrTiles] = total_tiles;
+    p.buf.hdr[kHdrBadSeqs] = total_bad;
   }
 }
 
@@ -288,7 +404,7 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
 }  // namespace
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanLanes), 0, stream, p);
   return hipGetLastError();
 }
 

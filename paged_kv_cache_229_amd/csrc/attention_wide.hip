@@ -77,6 +77,7 @@ attn_wide_kernel(const AttnParams p) {
   const int Hq = p.num_q_heads;
   const int total_items = p.buf.hdr[kHdrUnits] * Hkv;
   const int P = p.buf.hdr[kHdrPartition];
+  const int Pw = p.buf.hdr[kHdrPartitionWide];
   const int bs_log2 = p.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int last_block = static_cast<int>(p.num_blocks - 1);
@@ -122,15 +123,14 @@ attn_wide_kernel(const AttnParams p) {
     const int unit = item / Hkv;
     const int g = item - unit * Hkv;
     const int4 u = p.buf.units[unit];
-    const int s = u.x, tile = u.y, part = u.z, pbase = u.w;
+    const int s = u.x, tile = u.y, kb = u.z, pbase = u.w;
     const int q0 = p.query_start_loc[s];
     const int n = p.query_start_loc[s + 1] - q0;
     const int L = p.context_lens[s];
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;
-    const int kb = part * P;
-    const int ke = min(kmax, kb + P);
+    const int ke = min(kmax, kb + (rows_here > kSmallTileRows ? Pw : P));
     // Waves split the rows (WAVE_ROWS each) when there are enough, else the keys: WR row groups x WK key
     // groups.
     const int WR = rows_here <= T::WAVE_ROWS ? 1

@@ -23,7 +23,19 @@ constexpr int kDefaultItems = 1024;
 constexpr int kMinPartition = 256;
 
 // Workspace header words.
-enum HeaderWord { kHdrUnits = 0, kHdrQueue = 1, kHdrPartition = 2, kHdrTiles = 3, kHdrBadSeqs = 4 };
+enum HeaderWord {
+  kHdrUnits = 0,
+  kHdrQueue = 1,
+  kHdrPartition = 2,      // partition length of tiles with at most kSmallTileRows rows
+  kHdrTiles = 3,
+  kHdrBadSeqs = 4,
+  kHdrPartitionWide = 5,  // partition length of taller tiles
+};
+// Tiles with more rows than this (long query chunks) are split only over long contexts: their partial
+// rows cost as much to write and merge as a good share of the keys they would save reading, and there are
+// already many of them.  Their partition is at least kWidePartitionMin keys.
+constexpr int kSmallTileRows = 64;
+constexpr int kWidePartitionMin = 4096;
 
 // Device work plan, all in the caller's workspace.  A unit is (sequence, row tile, context partition);
 // every unit is processed once per kv head.
@@ -33,7 +45,7 @@ struct PlanBuffers {
   int* seq_units;   // [num_seqs]  scratch
   int* tile_base;   // [num_seqs + 1] first tile record of each sequence
   int4* tile_rec;   // [tile_cap]  {sequence, tile, first partial row or -1, number of partitions}
-  int4* units;      // [unit_cap]  {sequence, tile, partition, first partial row or -1 if unsplit}
+  int4* units;      // [unit_cap]  {sequence, tile, first key of the partition, first partial row or -1 if unsplit}
   float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
   float* part_acc;  // [prow_cap * head_dim] unnormalised partial outputs
 };
