@@ -160,6 +160,9 @@ def main() -> None:
     ap.add_argument("--tile-kind", type=int, default=0)
     ap.add_argument("--subset", choices=["all", "prefill", "decode"], default="all",
                     help="time only the sequences with q_len > 1 (prefill) or q_len == 1 (decode)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="pool layout [num_blocks, layers, block_size, H_kv, D] (layer inside the block), "
+                         "attending the last layer through block_stride; 1 = per-layer pool")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -209,6 +212,15 @@ def main() -> None:
 
     k0, v0 = t(w.k_pool), t(w.v_pool)
     copies = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(0, args.copies - 1))]
+    if args.layers > 1:
+        # Layer inside the block: each block holds every layer's rows; the attended layer's pool is a
+        # strided view (block_stride = layers * block_size * H_kv * D elements).
+        def inside(x):
+            big = torch.zeros((x.shape[0], args.layers) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+            big[:, args.layers - 1] = x
+            return big[:, args.layers - 1]
+        copies = [(inside(k), inside(v)) for k, v in copies]
+        k0, v0 = copies[0]
     bt = t(w.block_tables, False)
     q, kn, vn = t(st.q), t(st.k_new), t(st.v_new)
     sm, cl, qsl = t(st.slot_mapping, False), t(st.context_lens, False), t(st.query_start_loc, False)
@@ -266,7 +278,8 @@ def main() -> None:
                    "num_seqs": w.num_seqs,
                    "total_q": work["total_q"], "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "pool_copies": len(copies)},
+                   "pool_copies": len(copies),
+                   "pool_layout": "per_layer" if args.layers == 1 else f"layer_in_block x{args.layers}"},
         "tokens_per_s": round(work["total_q"] / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attention_kernel_ms": {"mean": round(k_avg, 5), "p10": round(float(np.percentile(kernel_ms, 10)), 5),

@@ -225,28 +225,32 @@ def test_shared_prefix_equals_private_copy():
     assert torch.equal(out1, out2)
 
 
-def test_layer_inside_block_pool():
-    """The pool layout [num_blocks, layers, block_size, H_kv, D] (layer inside the block) addressed
-    through block_stride gives the same result as the per-layer pool."""
-    w = make_config("decode", "small")
-    log("layer-inside-block pool")
+@pytest.mark.parametrize("workload,layers,layer", [("decode", 3, 1), ("decode", 2, 0), ("mixed", 4, 3),
+                                                   ("spec", 2, 1), ("tiny", 3, 2)])
+def test_layer_inside_block_pool(workload, layers, layer):
+    """The pool layout [num_blocks, layers, block_size, H_kv, D] (layer inside the block, "Paged
+    Attention 基础 – 原理与实现进度" §4) addressed through block_stride gives bit for bit the result and
+    the pool contents of the per-layer pool, and leaves the other layers untouched."""
+    w = make_config(workload, "small")
+    log(f"layer-inside-block pool {workload} layers={layers} layer={layer}")
     dw = DeviceWorkload(w)
-    layers, layer = 3, 1
     big_k = torch.zeros((w.num_blocks, layers) + tuple(dw.k_pool.shape[1:]), dtype=dw.k_pool.dtype,
                         device=dw.k_pool.device)
     big_v = torch.zeros_like(big_k)
     big_k[:, layer] = dw.k_pool
     big_v[:, layer] = dw.v_pool
-    out_ref = dw.run_step(0).clone()
-    st = dw.steps[0]
-    pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], big_k[:, layer], big_v[:, layer])
-    out = pkv.paged_attention_forward(st["q"], big_k[:, layer], big_v[:, layer], dw.block_tables,
-                                      st["context_lens"], st["query_start_loc"], scale=w.scale,
-                                       max_q_len=st["max_q_len"])
-    torch.cuda.synchronize()
-    assert torch.equal(out, out_ref)
-    assert torch.equal(big_k[:, layer], dw.k_pool)
-    assert int((big_k[:, 0] != 0).sum()) == 0 and int((big_k[:, 2] != 0).sum()) == 0
+    for i, st in enumerate(dw.steps):
+        out_ref = dw.run_step(i).clone()
+        pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], big_k[:, layer], big_v[:, layer])
+        out = pkv.paged_attention_forward(st["q"], big_k[:, layer], big_v[:, layer], dw.block_tables,
+                                          st["context_lens"], st["query_start_loc"], scale=w.scale,
+                                          max_q_len=st["max_q_len"])
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref)
+        assert torch.equal(big_k[:, layer], dw.k_pool) and torch.equal(big_v[:, layer], dw.v_pool)
+    for other in range(layers):
+        if other != layer:
+            assert int((big_k[:, other] != 0).sum()) == 0 and int((big_v[:, other] != 0).sum()) == 0
 
 
 def test_empty_and_degenerate():
