@@ -160,6 +160,9 @@ def main() -> None:
     ap.add_argument("--tile-kind", type=int, default=0)
     ap.add_argument("--subset", choices=["all", "prefill", "decode"], default="all",
                     help="time only the sequences with q_len > 1 (prefill) or q_len == 1 (decode)")
+    ap.add_argument("--prefix-pass", action="store_true",
+                    help="prefix workload: attend the shared blocks once for all sequences "
+                         "(paged_attention_forward_prefix)")
     ap.add_argument("--layers", type=int, default=1,
                     help="pool layout [num_blocks, layers, block_size, H_kv, D] (layer inside the block), "
                          "attending the last layer through block_stride; 1 = per-layer pool")
@@ -227,15 +230,29 @@ def main() -> None:
     max_q = int(np.diff(st.query_start_loc).max())
     out = torch.empty_like(q)
     pkv.set_tuning(args.partition, args.items, args.tile_kind)  # the workspace size depends on it
-    ws = torch.empty(max(256, pkv.workspace_size(w.num_seqs, q.shape[0], w.num_q_heads,
-                                                 w.num_kv_heads, w.head_dim, q.dtype, max_q)),
-                     dtype=torch.uint8, device=dev)
+    prefix_tokens = w.shared_prefix_blocks * w.block_size if args.prefix_pass else 0
+    if args.prefix_pass and prefix_tokens == 0:
+        print("bench.py: --prefix-pass needs a workload with shared prefix blocks (prefix)", file=sys.stderr)
+        sys.exit(2)
+    if prefix_tokens:
+        need = pkv.prefix_workspace_size(w.num_seqs, q.shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                         q.dtype)
+        kernel_name = "attn_wide_kernel"
+        traffic_key += ":prefix_pass"
+    else:
+        need = pkv.workspace_size(w.num_seqs, q.shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim, q.dtype,
+                                  max_q)
+    ws = torch.empty(max(256, need), dtype=torch.uint8, device=dev)
 
     def step(i):
         kp, vp = copies[i % len(copies)]
         pkv.paged_kv_write(kn, vn, sm, kp, vp)
-        pkv.paged_attention_forward(q, kp, vp, bt, cl, qsl, scale=w.scale, out=out, workspace=ws,
-                                    max_q_len=max_q)
+        if prefix_tokens:
+            pkv.paged_attention_forward_prefix(q, kp, vp, bt, cl, qsl, 0, w.num_seqs, prefix_tokens,
+                                               scale=w.scale, out=out, workspace=ws)
+        else:
+            pkv.paged_attention_forward(q, kp, vp, bt, cl, qsl, scale=w.scale, out=out, workspace=ws,
+                                        max_q_len=max_q)
 
     for i in range(args.warmup):
         step(i)
@@ -279,7 +296,8 @@ def main() -> None:
                    "total_q": work["total_q"], "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "pool_copies": len(copies),
-                   "pool_layout": "per_layer" if args.layers == 1 else f"layer_in_block x{args.layers}"},
+                   "pool_layout": "per_layer" if args.layers == 1 else f"layer_in_block x{args.layers}",
+                   "shared_prefix_pass": bool(prefix_tokens)},
         "tokens_per_s": round(work["total_q"] / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attention_kernel_ms": {"mean": round(k_avg, 5), "p10": round(float(np.percentile(kernel_ms, 10)), 5),

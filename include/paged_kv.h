@@ -14,6 +14,10 @@
  *                            model writes K/V into blocks, then reads through the paged call with the
  *                            per-layer slice k_cache[i]; Consequences: prefill and decode share one
  *                            multi-token call).
+ *   paged_attention_forward_prefix  the same result when a range of sequences shares its first blocks
+ *                            (the pages' prefix caching, §1 problem 3 and the §2 figure where two
+ *                            sequences start with one physical block): the shared keys are attended once
+ *                            for all sharers' query rows together.
  *   pkv_cm_* / paged_kv_copy_blocks  host cache manager (block allocator, block tables, slot mapping,
  *                            shared blocks with copy on write) and its device block copy (declared below).
  *
@@ -130,6 +134,45 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                             int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
                             int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Bytes of device workspace paged_attention_forward_prefix needs (0 for PKV_FP32).  Returns 0 and sets
+ * the last error on invalid arguments.
+ */
+size_t paged_attention_prefix_workspace_size(int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+
+/*
+ * paged_attention_forward_prefix — the result of paged_attention_forward (same arguments, same output up
+ * to float32 summation order), for a batch where sequences prefix_begin .. prefix_end - 1 share the
+ * physical blocks that hold their first prefix_tokens tokens (prefix caching, "Paged Attention 基础 –
+ * 原理与实现进度", §1 problem 3 and the §2 figure).  Instead of every sharer reading the shared blocks
+ * again, one pass attends all sharers' query rows to the shared keys at once (a dense contraction on the
+ * matrix cores); each sharer's own pass covers only its keys after the prefix, and the two partial
+ * softmax states (max, sum, unnormalised output) merge exactly as the split-context partitions do.
+ *
+ *   prefix_begin, prefix_end  0 <= prefix_begin <= prefix_end <= num_seqs (else PKV_ERR_INVALID_ARG);
+ *                 an empty range or prefix_tokens == 0 runs the ordinary computation.
+ *   prefix_tokens >= 0, a multiple of block_size and <= max_blocks_per_seq * block_size (else
+ *                 PKV_ERR_INVALID_ARG).  The caller promises that block_tables[s][0 .. prefix_tokens /
+ *                 block_size - 1] is the same for every s in the range (the sharing itself; the library
+ *                 does not compare tables, and a violation gives undefined output, like other metadata
+ *                 contents).  The device checks the rest and, if any sharer has a new token inside the
+ *                 prefix (context_lens[s] - n < prefix_tokens), holds more rows than one 256-row tile
+ *                 (n * num_q_heads / num_kv_heads > 256), or the extra work would not fit the workspace,
+ *                 runs the ordinary computation instead.
+ *   workspace     at least paged_attention_prefix_workspace_size() bytes, 256-byte aligned.
+ * Everything else as paged_attention_forward (which picks the row tile from max_q_len_hint; this call
+ * always uses 256-row tiles).  PKV_FP32 runs the ordinary fp32 computation.
+ */
+int paged_attention_forward_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, const int32_t* query_start_loc,
+                                   int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
+                                   int32_t prefix_begin, int32_t prefix_end, int32_t prefix_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_kv_copy_blocks — for i < num_pairs: block dst_blocks[i] of both caches takes the contents of

@@ -40,7 +40,9 @@ from ._native import (  # noqa: F401
 __all__ = [
     "paged_kv_write",
     "paged_attention_forward",
+    "paged_attention_forward_prefix",
     "workspace_size",
+    "prefix_workspace_size",
     "set_tuning",
     "set_profile_events",
     "validate_metadata",
@@ -121,17 +123,17 @@ def workspace_size(num_seqs: int, total_q: int, num_q_heads: int, num_kv_heads: 
     return int(n)
 
 
-def paged_attention_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                            block_tables: torch.Tensor, context_lens: torch.Tensor,
-                            query_start_loc: torch.Tensor, scale: float | None = None,
-                            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                            max_q_len: int | None = None, validate: bool = False) -> torch.Tensor:
-    """Causal paged attention; see ``paged_attention_forward`` in include/paged_kv.h.
+def prefix_workspace_size(num_seqs: int, total_q: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          dtype: torch.dtype) -> int:
+    n = lib().paged_attention_prefix_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                                    _DTYPES[dtype])
+    err = lib().paged_kv_last_error()
+    if err:
+        raise PagedKVError(PKV_ERR_INVALID_ARG, err.decode())
+    return int(n)
 
-    ``q`` ``[total_q, H_q, D]`` packs each sequence's new tokens at ``query_start_loc[s] :
-    query_start_loc[s+1]``; ``context_lens[s]`` counts every cached token including them.  ``scale``
-    defaults to ``1/sqrt(D)``.  ``workspace`` (uint8, device) is allocated when not given.  Returns
-    ``out`` ``[total_q, H_q, D]`` in q's dtype.  Asynchronous on the current stream."""
+
+def _attention_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, validate):
     dev = _same_device(q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
     nb, bs, hkv, d, stride = _pool_geometry(k_cache, v_cache)
     if q.dim() != 3 or q.shape[2] != d or not q.is_contiguous():
@@ -156,18 +158,63 @@ def paged_attention_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         validate_metadata(block_tables=block_tables, context_lens=context_lens,
                           query_start_loc=query_start_loc, num_blocks=nb, block_size=bs,
                           total_q=total_q)
-    code = _dtype_code(q)
-    hint = -1 if max_q_len is None else int(max_q_len)
-    need = workspace_size(num_seqs, total_q, hq, hkv, d, q.dtype, max_q_len)
+    return dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, float(scale)
+
+
+def _workspace(workspace, need, dev):
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    elif workspace.device != dev or workspace.dtype != torch.uint8:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8:
         raise ValueError("workspace must be a uint8 tensor on q's device")
+    return workspace
+
+
+def paged_attention_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            query_start_loc: torch.Tensor, scale: float | None = None,
+                            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            max_q_len: int | None = None, validate: bool = False) -> torch.Tensor:
+    """Causal paged attention; see ``paged_attention_forward`` in include/paged_kv.h.
+
+    ``q`` ``[total_q, H_q, D]`` packs each sequence's new tokens at ``query_start_loc[s] :
+    query_start_loc[s+1]``; ``context_lens[s]`` counts every cached token including them.  ``scale``
+    defaults to ``1/sqrt(D)``.  ``workspace`` (uint8, device) is allocated when not given.  Returns
+    ``out`` ``[total_q, H_q, D]`` in q's dtype.  Asynchronous on the current stream."""
+    dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, scale = _attention_args(
+        q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, validate)
+    hint = -1 if max_q_len is None else int(max_q_len)
+    workspace = _workspace(workspace, workspace_size(num_seqs, total_q, hq, hkv, d, q.dtype, max_q_len), dev)
     check(lib().paged_attention_forward(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q,
-        hq, hkv, d, bs, nb, stride, float(scale), code, hint, workspace.data_ptr(),
+        hq, hkv, d, bs, nb, stride, scale, _dtype_code(q), hint, workspace.data_ptr(),
         workspace.numel(), _stream(dev)))
+    return out
+
+
+def paged_attention_forward_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   query_start_loc: torch.Tensor, prefix_begin: int, prefix_end: int,
+                                   prefix_tokens: int, scale: float | None = None,
+                                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                   validate: bool = False) -> torch.Tensor:
+    """``paged_attention_forward`` for a batch whose sequences ``prefix_begin .. prefix_end - 1`` share the
+    blocks of their first ``prefix_tokens`` tokens: the shared keys are attended once for all of them.
+    Same result; see ``paged_attention_forward_prefix`` in include/paged_kv.h.  ``validate`` also checks
+    on the host that the range's block tables agree over the prefix."""
+    dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, scale = _attention_args(
+        q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, validate)
+    if validate and prefix_tokens > 0 and prefix_end > prefix_begin:
+        nblk = -(-int(prefix_tokens) // bs)
+        rows = block_tables[prefix_begin:prefix_end, :nblk].cpu()
+        if not bool((rows == rows[0:1]).all()):
+            raise ValueError("the prefix range's block tables differ over the prefix")
+    workspace = _workspace(workspace, prefix_workspace_size(num_seqs, total_q, hq, hkv, d, q.dtype), dev)
+    check(lib().paged_attention_forward_prefix(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q,
+        hq, hkv, d, bs, nb, stride, scale, _dtype_code(q), int(prefix_begin), int(prefix_end),
+        int(prefix_tokens), workspace.data_ptr(), workspace.numel(), _stream(dev)))
     return out
 
 

@@ -203,6 +203,7 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
       p.buf.hdr[kHdrPartitionWide] = kStageKeys;
       p.buf.hdr[kHdrTiles] = 0;
       p.buf.hdr[kHdrBadSeqs] = -1;
+      p.buf.hdr[kHdrPrefN] = 0;
     }
     return;
   }
@@ -221,6 +222,53 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
   }
   auto wide_len = [&](int P_) { return p.forced_partition > 0 ? P_ : min(max(P_, kWidePartitionMin), pmax); };
 
+  // Shared-prefix pass: on only when every member sequence is valid, fits one tile and has all of its new
+  // tokens after the prefix, and when the extra units and partial rows fit; otherwise the ordinary plan.
+  const int pb = p.prefix.begin, pe = p.prefix.end, ptok = p.prefix.tokens;
+  bool pref = ptok > 0 && pb >= 0 && pe > pb && pe <= N;
+  int vq0 = 0, vn = 0, tiles_v = 0, npv = 0, Pv = 0;
+  if (pref) {
+    int viol = 0;
+    for (int s = pb + lane; s < pe; s += kPlanLanes) {
+      int n, L;
+      const int nt = seq(s, n, L);
+      if (n < 0 || (n > 0 && (nt != 1 || L - n < ptok))) ++viol;
+    }
+    viol = wave_sum(viol);
+    vq0 = qsl[pb];
+    vn = qsl[pe] - vq0;
+    pref = viol == 0 && vn > 0;
+    if (pref) {
+      tiles_v = (vn * G + RT - 1) / RT;
+      if (p.forced_partition > 0) {
+        Pv = P;
+      } else {
+        // about one prefix item per CU, partitions of at least 256 keys
+        const int want = min(max(1, (256 + tiles_v * Hkv - 1) / (tiles_v * Hkv)), max(1, ptok / 256));
+        Pv = ((ptok + want - 1) / want + kStageKeys - 1) / kStageKeys * kStageKeys;
+      }
+      npv = (ptok + Pv - 1) / Pv;
+      const long long min_prows = static_cast<long long>(1 + npv) * vn * G * Hkv;
+      pref = static_cast<long long>(tiles_v) * npv <= p.unit_cap - p.tile_cap && min_prows <= p.prow_cap;
+    }
+    if (!pref) vn = tiles_v = npv = 0;
+  }
+  const int units_v = tiles_v * npv;
+
+  // Partitions of tile t of sequence s for partition lengths (P_, Pw_): own key range starts at *k0
+  // (after the prefix for members of the shared-prefix pass), *np_own partitions of *len keys over it;
+  // returns all partitions of the tile including the prefix ones.
+  auto tile_parts = [&](int s, int n, int L, int rows, int t, int P_, int Pw_, const FastDiv& dp,
+                        const FastDiv& dw, int& len, int& k0, int& np_own) -> int {
+    const int rows_t = min(RT, rows - t * RT);
+    const int km = geo.kmax(L, n, rows, t);
+    const bool member = pref && s >= pb && s < pe;
+    k0 = member ? ptok : 0;
+    len = rows_t > kSmallTileRows ? Pw_ : P_;
+    np_own = rows_t > kSmallTileRows ? dw.ceil_div(km - k0) : dp.ceil_div(km - k0);
+    return np_own + (member ? npv : 0);
+  };
+
   // Lengthen P until the units and the split tiles' partial rows fit the workspace.
   int units_total = 0;
   for (;;) {
@@ -232,14 +280,13 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
       const int nt = seq(s, n, L);
       const int rows = n * G;
       for (int t = 0; t < nt; ++t) {
-        const int rows_t = min(RT, rows - t * RT);
-        const int km = geo.kmax(L, n, rows, t);
-        const int np = rows_t > kSmallTileRows ? divw.ceil_div(km) : divp.ceil_div(km);
-        units = min(units + np, kSat);
-        if (np > 1) prows = min(prows + min(np * rows_t, kSat) * Hkv, kSat);
+        int len, k0, np_own;
+        const int np = tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
+        units = min(units + np_own, kSat);
+        if (np > 1) prows = min(prows + min(np * min(RT, rows - t * RT), kSat) * Hkv, kSat);
       }
     }
-    units_total = wave_sum(units);
+    units_total = wave_sum(units) + units_v;
     const int prows_total = wave_sum(prows);
     if ((units_total <= p.unit_cap && prows_total <= p.prow_cap) || P >= max_kmax) break;
     P = P > pmax / 2 ? pmax : 2 * P;
@@ -247,11 +294,6 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
 
   const int Pw = wide_len(P);
   const FastDiv divp(P), divw(Pw);
-  // Partition length and count of tile t of a sequence.
-  auto split = [&](int rows_t, int km, int& len) {
-    len = rows_t > kSmallTileRows ? Pw : P;
-    return rows_t > kSmallTileRows ? divw.ceil_div(km) : divp.ceil_div(km);
-  };
   // First partial row of every sequence's split tiles, in sequence order.
   {
     int run = 0;
@@ -263,10 +305,9 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
         const int nt = seq(s, n, L);
         const int rows = n * G;
         for (int t = 0; t < nt; ++t) {
-          const int rows_t = min(RT, rows - t * RT);
-          int len;
-          const int np = split(rows_t, geo.kmax(L, n, rows, t), len);
-          if (np > 1) pr += np * rows_t * Hkv;
+          int len, k0, np_own;
+          const int np = tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
+          if (np > 1) pr += np * min(RT, rows - t * RT) * Hkv;
         }
       }
       int sum;
@@ -286,10 +327,15 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
     const int nt = seq(s, n, L);
     const int rows = n * G;
     for (int t = 0; t < nt; ++t) {
+      int len, k0, np_own;
+      tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
       const int km = geo.kmax(L, n, rows, t);
-      const int len = min(RT, rows - t * RT) > kSmallTileRows ? Pw : P;
-      for (int k0 = 0; k0 < km; k0 += len) atomicAdd(&bucket[sort_bucket(min(km - k0, len))], 1);
+      for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len))], 1);
     }
+  }
+  for (int i = lane; i < units_v; i += kPlanLanes) {
+    const int k = (i % npv) * Pv;
+    atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
   }
   __syncthreads();
   {
@@ -320,17 +366,29 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
     for (int t = 0; t < nt; ++t) {
       const int km = geo.kmax(L, n, rows, t);
       const int rows_t = min(RT, rows - t * RT);
-      int len;
-      const int np = split(rows_t, km, len);
+      int len, k0, np_own;
+      const int np = tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
       p.buf.tile_rec[tb] = make_int4(s, t, np > 1 ? pr : -1, np);
       ++tb;
-      for (int pp = 0; pp < np; ++pp) {
-        const int k0 = pp * len;
-        const int slot = atomicAdd(&bucket[sort_bucket(min(km - k0, len))], 1);
-        p.buf.units[slot] = make_int4(s, t, k0, np > 1 ? pr + pp * rows_t * Hkv : -1);
+      for (int pp = 0; pp < np_own; ++pp) {
+        const int kb = k0 + pp * len;
+        const int slot = atomicAdd(&bucket[sort_bucket(min(km - kb, len))], 1);
+        p.buf.units[slot] = make_int4(s, t, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
+      }
+      if (np > np_own) {
+        // member of the shared-prefix pass: its query tokens find their prefix partial rows here
+        const int q_lo = qsl[s];
+        const int4 info = make_int4(s, pr + np_own * rows_t * Hkv, rows_t, q_lo);
+        for (int i = 0; i < n; ++i) p.buf.tok_info[q_lo - vq0 + i] = info;
       }
       if (np > 1) pr += np * rows_t * Hkv;
     }
+  }
+  for (int i = lane; i < units_v; i += kPlanLanes) {
+    const int tv = i / npv;
+    const int k = (i - tv * npv) * Pv;
+    const int slot = atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
+    p.buf.units[slot] = make_int4(N, tv, k, -1);
   }
   if (lane == 0) {
     p.buf.tile_base[N] = total_tiles;
@@ -340,6 +398,13 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
     p.buf.hdr[kHdrPartitionWide] = Pw;
     p.buf.hdr[kHdrTiles] = total_tiles;
     p.buf.hdr[kHdrBadSeqs] = total_bad;
+    p.buf.hdr[kHdrPrefQ0] = vq0;
+    p.buf.hdr[kHdrPrefN] = vn;
+    p.buf.hdr[kHdrPrefL] = ptok - 1 + vn;
+    p.buf.hdr[kHdrPrefKeys] = ptok;
+    p.buf.hdr[kHdrPrefTable] = pb;
+    p.buf.hdr[kHdrPrefPartition] = Pv;
+    p.buf.hdr[kHdrPrefParts] = npv;
   }
 }
 

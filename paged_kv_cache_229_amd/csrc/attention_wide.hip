@@ -78,6 +78,13 @@ attn_wide_kernel(const AttnParams p) {
   const int total_items = p.buf.hdr[kHdrUnits] * Hkv;
   const int P = p.buf.hdr[kHdrPartition];
   const int Pw = p.buf.hdr[kHdrPartitionWide];
+  // Shared-prefix sequence (index num_seqs in the unit records; absent when it has no tokens).
+  const int pre_q0 = p.buf.hdr[kHdrPrefQ0];
+  const int pre_n = p.buf.hdr[kHdrPrefN];
+  const int pre_L = p.buf.hdr[kHdrPrefL];
+  const int pre_keys = p.buf.hdr[kHdrPrefKeys];
+  const int pre_table = p.buf.hdr[kHdrPrefTable];
+  const int pre_P = p.buf.hdr[kHdrPrefPartition];
   const int bs_log2 = p.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int last_block = static_cast<int>(p.num_blocks - 1);
@@ -124,13 +131,18 @@ attn_wide_kernel(const AttnParams p) {
     const int g = item - unit * Hkv;
     const int4 u = p.buf.units[unit];
     const int s = u.x, tile = u.y, kb = u.z, pbase = u.w;
-    const int q0 = p.query_start_loc[s];
-    const int n = p.query_start_loc[s + 1] - q0;
-    const int L = p.context_lens[s];
+    // The shared-prefix sequence: its query tokens are the member sequences' and every prefix key is
+    // visible to each of them (context pre_L = prefix length - 1 + token count); its rows' results are
+    // partial rows of the members' tiles.
+    const bool pre = s == p.num_seqs;
+    const int q0 = pre ? pre_q0 : p.query_start_loc[s];
+    const int n = pre ? pre_n : p.query_start_loc[s + 1] - q0;
+    const int L = pre ? pre_L : p.context_lens[s];
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;
-    const int ke = min(kmax, kb + (rows_here > kSmallTileRows ? Pw : P));
+    const int ke = pre ? min(min(kmax, kb + pre_P), pre_keys) : min(kmax, kb + (rows_here > kSmallTileRows ? Pw : P));
+    const int pre_part = pre ? kb / pre_P : 0;  // partition of the prefix sequence
     // Waves split the rows (WAVE_ROWS each) when there are enough, else the keys: WR row groups x WK key
     // groups.
     const int WR = rows_here <= T::WAVE_ROWS ? 1
@@ -147,7 +159,7 @@ attn_wide_kernel(const AttnParams p) {
     const int lim0 = min(L - n + my_row0 / G, ke - 1);
     const int limw = min(L - n + (min(my_row0 + 32 * nh, row0 + rows_here) - 1) / G, ke - 1);
     const CONST_AS int* const tbl =
-        (const CONST_AS int*)(p.block_tables + static_cast<int64_t>(s) * p.max_blocks_per_seq);
+        (const CONST_AS int*)(p.block_tables + static_cast<int64_t>(pre ? pre_table : s) * p.max_blocks_per_seq);
     const int nst = (ke - kb + kStageKeys - 1) / kStageKeys;
 
     // Physical blocks of this wave's NL loads of stage st (scalar loads; keys past ke clamp to ke-1).
@@ -346,7 +358,7 @@ attn_wide_kernel(const AttnParams p) {
       if (r >= row0 + rows_here) return;
       const int ri = r / G;
       const int rh = r - ri * G;
-      if (pbase < 0) {
+      if (pbase < 0 && !pre) {
         const float inv = 1.f / ll;
         __bf16* const o = og + ((static_cast<int64_t>(q0 + ri) * Hq + g * G + rh) * D + 32 * dt + 4 * hf);
 #pragma unroll
@@ -357,7 +369,15 @@ attn_wide_kernel(const AttnParams p) {
           *reinterpret_cast<bf16x4*>(o + 8 * i4) = v;
         }
       } else {
-        const int64_t prow = static_cast<int64_t>(pbase) + g * rows_here + (r - row0);
+        int64_t prow;
+        if (pre) {
+          // token ri of the prefix sequence belongs to member info.x, whose tile keeps this partition's
+          // partial rows from info.y on: partition pre_part, kv head g, the member's row
+          const int4 info = p.buf.tok_info[ri];
+          prow = static_cast<int64_t>(info.y) + (pre_part * Hkv + g) * info.z + (q0 + ri - info.w) * G + rh;
+        } else {
+          prow = static_cast<int64_t>(pbase) + g * rows_here + (r - row0);
+        }
         float* const pa = p.buf.part_acc + prow * D + 32 * dt + 4 * hf;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 thread_local std::string g_error;
 thread_local int g_partition_keys = 0;
@@ -82,7 +82,7 @@ int check_pool(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_
 }
 
 struct WsLayout {
-  size_t hdr, seq_tiles, seq_units, tile_base, tile_rec, units, part_ml, part_acc, total;
+  size_t hdr, seq_tiles, seq_units, tile_base, tile_rec, units, part_ml, part_acc, tok_info, total;
   int rows_per_tile;
   int64_t tile_cap, unit_cap;
 };
@@ -102,7 +102,9 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   w.rows_per_tile = pkv::tile_rows_of(tile_kind);
   // Each sequence adds at most one partly filled tile.
   w.tile_cap = (total_q * group + w.rows_per_tile - 1) / w.rows_per_tile + num_seqs;
-  w.unit_cap = (pkv::kMaxItems + num_kv_heads - 1) / num_kv_heads + w.tile_cap;
+  // Room for the items, one unit per tile when nothing is split, and a shared-prefix pass (at most about
+  // 256 items plus one per prefix tile).
+  w.unit_cap = (pkv::kMaxItems + num_kv_heads - 1) / num_kv_heads + 2 * w.tile_cap + 256;
   size_t off = 0;
   w.hdr = off;
   off = round256(off + 16 * sizeof(int));
@@ -121,6 +123,8 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   off = round256(off + part_rows * 2 * sizeof(float));
   w.part_acc = off;
   off = round256(off + part_rows * head_dim * sizeof(float));
+  w.tok_info = off;
+  off = round256(off + static_cast<size_t>(total_q) * 4 * sizeof(int));
   w.total = off;
   return w;
 }
@@ -228,14 +232,18 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int64_t total_q, int32_t
       .total;
 }
 
-int paged_attention_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                            const int32_t* context_lens, const int32_t* query_start_loc,
-                            int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                            int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
-                            int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both attention entry points.  `prefix` enables the shared-prefix pass (and the 256-row tiles it runs
+// on); its range was checked by the caller.
+int attention_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                   const int32_t* query_start_loc, int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int64_t block_stride, float scale, int32_t dtype, int32_t max_q_len_hint,
+                   const pkv::PrefixParams* prefix, void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || total_q < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs and total_q must be >= 0");
   int64_t stride = 0;
   const int rc = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
@@ -286,7 +294,7 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
     return succeed();
   }
 
-  const int tile_kind = choose_tile_kind(group, total_q, max_q_len_hint);
+  const int tile_kind = prefix ? 2 : choose_tile_kind(group, total_q, max_q_len_hint);
   const WsLayout w = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind);
   if (!workspace || workspace_bytes < w.total)
     return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(w.total) + " bytes, got " +
@@ -302,6 +310,7 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
   b.units = reinterpret_cast<int4*>(ws + w.units);
   b.part_ml = reinterpret_cast<float2*>(ws + w.part_ml);
   b.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
+  b.tok_info = reinterpret_cast<int4*>(ws + w.tok_info);
   p.buf = b;
   p.rows_per_tile = w.rows_per_tile;
 
@@ -321,6 +330,7 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
   pp.unit_cap = static_cast<int>(w.unit_cap);
   pp.tile_cap = static_cast<int>(w.tile_cap);
   pp.prow_cap = pkv::kPartialRowCap;
+  if (prefix) pp.prefix = *prefix;
   pp.buf = b;
 
   hipError_t e = pkv::launch_plan(pp, st);
@@ -335,6 +345,57 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
   e = pkv::launch_split_reduce(p, head_dim, static_cast<int>(w.tile_cap), st);
   if (e != hipSuccess) return hip_fail("split reduce launch", e);
   return succeed();
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* query_start_loc,
+                            int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
+                            int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, block_stride, scale, dtype, max_q_len_hint, nullptr, workspace,
+                        workspace_bytes, stream);
+}
+
+size_t paged_attention_prefix_workspace_size(int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+  if (num_seqs < 0 || total_q < 0 || num_kv_heads < 1 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) ||
+      (dtype != PKV_FP32 && dtype != PKV_BF16)) {
+    fail(PKV_ERR_INVALID_ARG, "invalid sizes for paged_attention_prefix_workspace_size");
+    return 0;
+  }
+  g_error.clear();
+  if (dtype == PKV_FP32 || num_seqs == 0 || total_q == 0) return 0;
+  return workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, 2).total;
+}
+
+int paged_attention_forward_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, const int32_t* query_start_loc,
+                                   int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
+                                   int32_t prefix_begin, int32_t prefix_end, int32_t prefix_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (prefix_begin < 0 || prefix_end < prefix_begin || prefix_end > num_seqs || prefix_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "need 0 <= prefix_begin <= prefix_end <= num_seqs and prefix_tokens >= 0");
+  if (block_size > 0 && prefix_tokens % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG, "prefix_tokens must be a multiple of block_size");
+  if (static_cast<int64_t>(prefix_tokens) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "prefix_tokens exceeds max_blocks_per_seq * block_size");
+  const pkv::PrefixParams pre{prefix_begin, prefix_end, prefix_tokens};
+  return attention_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, block_stride, scale, dtype, 0, &pre, workspace, workspace_bytes, stream);
 }
 
 int paged_attention_set_tuning(int32_t partition_keys, int32_t target_items, int32_t tile_kind) {

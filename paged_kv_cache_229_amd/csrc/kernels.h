@@ -30,6 +30,16 @@ enum HeaderWord {
   kHdrTiles = 3,
   kHdrBadSeqs = 4,
   kHdrPartitionWide = 5,  // partition length of taller tiles
+  // Shared-prefix pass (0 rows when off): the prefix sequence's first query token, token count, context
+  // (prefix length - 1 + token count, so every prefix key is visible to every row), key end (the prefix
+  // length), block-table row, partition length and partition count.
+  kHdrPrefQ0 = 6,
+  kHdrPrefN = 7,
+  kHdrPrefL = 8,
+  kHdrPrefKeys = 9,
+  kHdrPrefTable = 10,
+  kHdrPrefPartition = 11,
+  kHdrPrefParts = 12,
 };
 // Tiles with more rows than this (long query chunks) are split only over long contexts: their partial
 // rows cost as much to write and merge as a good share of the keys they would save reading, and there are
@@ -48,6 +58,20 @@ struct PlanBuffers {
   int4* units;      // [unit_cap]  {sequence, tile, first key of the partition, first partial row or -1 if unsplit}
   float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
   float* part_acc;  // [prow_cap * head_dim] unnormalised partial outputs
+  // [total_q] for query tokens of the shared-prefix sequences: {sequence, first partial row of its
+  // shared-prefix partitions, its rows, its first query token}
+  int4* tok_info;
+};
+
+// Shared-prefix pass.  Sequences [prefix_begin, prefix_end) share the blocks holding their first
+// prefix_tokens tokens.  The plan adds one prefix sequence (index num_seqs in the unit records) whose
+// query tokens are all of theirs and whose keys are the prefix, all visible to every row; each member's
+// own units cover keys [prefix_tokens, kmax), and the prefix sequence's partitions write partial rows
+// into extra partitions of the members' tiles, which split_reduce_kernel merges with the rest.
+struct PrefixParams {
+  int begin;
+  int end;
+  int tokens;  // 0 = no shared-prefix pass
 };
 
 // Partial rows of a split unit u (tile with `rows` rows): [u.w, u.w + H_kv * rows), kv head g's rows at
@@ -68,6 +92,7 @@ struct PlanParams {
   int unit_cap;
   int tile_cap;
   int prow_cap;
+  PrefixParams prefix;
   PlanBuffers buf;
 };
 
