@@ -27,14 +27,13 @@
 namespace pkv {
 namespace {
 
-// One wave plans the whole call: every step is a per-lane loop over sequences s = lane, lane + 64, ...
-// followed by wave reductions or scans, so the kernel needs no workgroup barrier.  Each sequence's
+// One workgroup plans the whole call (one wave for up to 128 sequences, four waves beyond): every step is
+// a per-thread loop over sequences s = tid, tid + THREADS, ... followed by a reduction or scan (DPP
+// inside each wave, then the wave totals through LDS).  Each sequence's
 // (new tokens, context, tiles) is read from global memory once and kept in LDS (for the first
 // kSeqCache sequences; later ones are read again), and all arithmetic is 32-bit: 64-bit division is a
 // long software routine on this GPU.
-constexpr int kPlanLanes = 64;
 constexpr int kSortBuckets = 1024;
-constexpr int kBucketsPerLane = kSortBuckets / kPlanLanes;
 constexpr int kSeqCache = 2048;
 
 __device__ inline bool seq_ok(int q_lo, int q_hi, int context_len, int64_t total_q, int max_context) {
@@ -95,13 +94,6 @@ __device__ inline int wave_inclusive_scan(int v) {
   return v;
 }
 
-// Exclusive prefix sum over the lanes; *total receives the sum of all lanes.
-__device__ inline int wave_exclusive_scan(int v, int* total) {
-  const int incl = wave_inclusive_scan(v);
-  *total = __builtin_amdgcn_readlane(incl, 63);
-  return incl - v;
-}
-
 __device__ inline int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_inclusive_scan(v), 63); }
 
 __device__ inline int wave_max(int v) {
@@ -115,11 +107,59 @@ __device__ inline int wave_max(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-__global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
+// Workgroup-wide versions (every thread calls them; `red` holds kPlanWaves ints of LDS).
+template <int WAVES>
+__device__ inline int block_sum(int v, int* red) {
+  const int w = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+template <int WAVES>
+__device__ inline int block_max(int v, int* red) {
+  const int w = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) t = max(t, red[i]);
+  __syncthreads();
+  return t;
+}
+
+template <int WAVES>
+__device__ inline int block_exclusive_scan(int v, int* total, int* red) {
+  const int incl = wave_inclusive_scan(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) red[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) {
+    const int x = red[i];
+    before += i < wave ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+template <int THREADS>
+__global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
+  constexpr int kPlanThreads = THREADS;
+  constexpr int kPlanWaves = THREADS / 64;
+  constexpr int kBucketsPerThread = kSortBuckets / THREADS;
   __shared__ int bucket[kSortBuckets];
   __shared__ int4 seqc[kSeqCache];  // (n, L, tiles, first partial row) per sequence
   __shared__ int tbase[kSeqCache];  // first tile record per sequence
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ int red[kPlanWaves];
   const int N = p.num_seqs;
   const int RT = p.rows_per_tile;
   const int G = p.group;
@@ -127,9 +167,9 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
   const int* const qsl = p.query_start_loc;
   const int* const ctx = p.context_lens;
   const TileGeom geo{G, RT, RT % G == 0 ? RT / G : 0};
-  // Per-lane partial counts only ever meet caps below 2^17; saturating them keeps every wave sum in
-  // 32 bits.
-  constexpr int kSat = 1 << 24;
+  // Per-thread partial counts only ever meet caps below 2^17; saturating them at 2^22 keeps every
+  // workgroup sum (256 threads) in 32 bits.
+  constexpr int kSat = 1 << 22;
 
   // (n, L, tiles) of sequence s; tiles is 0 for empty or invalid sequences.
   auto seq = [&](int s, int& n, int& L) -> int {
@@ -148,11 +188,11 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
   // Stage (first query, one past the last query, context) of the cached sequences in LDS; unrolled so
   // that many loads are in flight at once.
 #pragma unroll 8
-  for (int s = lane; s < min(N, kSeqCache); s += kPlanLanes) seqc[s] = make_int4(qsl[s], qsl[s + 1], ctx[s], 0);
+  for (int s = tid; s < min(N, kSeqCache); s += kPlanThreads) seqc[s] = make_int4(qsl[s], qsl[s + 1], ctx[s], 0);
 
   // Tiles per sequence, key work (in 64-key stages), longest context.
   int work = 0, bad = 0, maxk = 0;
-  for (int s = lane; s < N; s += kPlanLanes) {
+  for (int s = tid; s < N; s += kPlanThreads) {
     int lo, hi, L;
     if (s < kSeqCache) {
       const int4 c = seqc[s];
@@ -177,18 +217,18 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
     if (s < kSeqCache) seqc[s] = make_int4(n, L, nt, 0);
     else p.buf.seq_tiles[s] = nt;
   }
-  const long long total_work = static_cast<long long>(wave_sum(work)) * kStageKeys;
-  const int total_bad = wave_sum(bad);
-  const int max_kmax = wave_max(maxk);
+  const long long total_work = static_cast<long long>(block_sum<kPlanWaves>(work, red)) * kStageKeys;
+  const int total_bad = block_sum<kPlanWaves>(bad, red);
+  const int max_kmax = block_max<kPlanWaves>(maxk, red);
 
   // First tile record of every sequence, in sequence order.
   int total_tiles = 0;
-  for (int base = 0; base < N; base += kPlanLanes) {
-    const int s = base + lane;
+  for (int base = 0; base < N; base += kPlanThreads) {
+    const int s = base + tid;
     int n, L;
     const int nt = s < N ? seq(s, n, L) : 0;
     int sum;
-    const int first = total_tiles + wave_exclusive_scan(nt, &sum);
+    const int first = total_tiles + block_exclusive_scan<kPlanWaves>(nt, &sum, red);
     if (s < kSeqCache) tbase[s] = first;
     if (s < N) p.buf.tile_base[s] = first;
     total_tiles += sum;
@@ -196,7 +236,7 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
   }
 
   if (total_tiles > p.tile_cap) {  // inconsistent metadata: do nothing
-    if (lane == 0) {
+    if (tid == 0) {
       p.buf.hdr[kHdrUnits] = 0;
       p.buf.hdr[kHdrQueue] = 0;
       p.buf.hdr[kHdrPartition] = kStageKeys;
@@ -229,12 +269,12 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
   int vq0 = 0, vn = 0, tiles_v = 0, npv = 0, Pv = 0;
   if (pref) {
     int viol = 0;
-    for (int s = pb + lane; s < pe; s += kPlanLanes) {
+    for (int s = pb + tid; s < pe; s += kPlanThreads) {
       int n, L;
       const int nt = seq(s, n, L);
       if (n < 0 || (n > 0 && (nt != 1 || L - n < ptok))) ++viol;
     }
-    viol = wave_sum(viol);
+    viol = block_sum<kPlanWaves>(viol, red);
     vq0 = qsl[pb];
     vn = qsl[pe] - vq0;
     pref = viol == 0 && vn > 0;
@@ -275,7 +315,7 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
     const int Pw = wide_len(P);
     const FastDiv divp(P), divw(Pw);
     int units = 0, prows = 0;
-    for (int s = lane; s < N; s += kPlanLanes) {
+    for (int s = tid; s < N; s += kPlanThreads) {
       int n, L;
       const int nt = seq(s, n, L);
       const int rows = n * G;
@@ -286,8 +326,8 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
         if (np > 1) prows = min(prows + min(np * min(RT, rows - t * RT), kSat) * Hkv, kSat);
       }
     }
-    units_total = wave_sum(units) + units_v;
-    const int prows_total = wave_sum(prows);
+    units_total = block_sum<kPlanWaves>(units, red) + units_v;
+    const int prows_total = block_sum<kPlanWaves>(prows, red);
     if ((units_total <= p.unit_cap && prows_total <= p.prow_cap) || P >= max_kmax) break;
     P = P > pmax / 2 ? pmax : 2 * P;
   }
@@ -297,8 +337,8 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
   // First partial row of every sequence's split tiles, in sequence order.
   {
     int run = 0;
-    for (int base = 0; base < N; base += kPlanLanes) {
-      const int s = base + lane;
+    for (int base = 0; base < N; base += kPlanThreads) {
+      const int s = base + tid;
       int pr = 0;
       if (s < N) {
         int n, L;
@@ -311,7 +351,7 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
         }
       }
       int sum;
-      const int first = run + wave_exclusive_scan(pr, &sum);
+      const int first = run + block_exclusive_scan<kPlanWaves>(pr, &sum, red);
       if (s < kSeqCache) seqc[s].w = first;
       else if (s < N) p.buf.seq_units[s] = first;
       run += sum;
@@ -320,9 +360,9 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
 
   // Counting sort of the units by stage count, longest first: histogram, bucket offsets, scatter.
 #pragma unroll
-  for (int i = 0; i < kBucketsPerLane; ++i) bucket[lane * kBucketsPerLane + i] = 0;
+  for (int i = 0; i < kBucketsPerThread; ++i) bucket[tid * kBucketsPerThread + i] = 0;
   __syncthreads();
-  for (int s = lane; s < N; s += kPlanLanes) {
+  for (int s = tid; s < N; s += kPlanThreads) {
     int n, L;
     const int nt = seq(s, n, L);
     const int rows = n * G;
@@ -333,30 +373,30 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
       for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len))], 1);
     }
   }
-  for (int i = lane; i < units_v; i += kPlanLanes) {
+  for (int i = tid; i < units_v; i += kPlanThreads) {
     const int k = (i % npv) * Pv;
     atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
   }
   __syncthreads();
   {
-    int c[kBucketsPerLane];
+    int c[kBucketsPerThread];
     int mine = 0;
 #pragma unroll
-    for (int i = 0; i < kBucketsPerLane; ++i) {
-      c[i] = bucket[lane * kBucketsPerLane + i];
+    for (int i = 0; i < kBucketsPerThread; ++i) {
+      c[i] = bucket[tid * kBucketsPerThread + i];
       mine += c[i];
     }
     int dummy;
-    int off = wave_exclusive_scan(mine, &dummy);
+    int off = block_exclusive_scan<kPlanWaves>(mine, &dummy, red);
 #pragma unroll
-    for (int i = 0; i < kBucketsPerLane; ++i) {
-      bucket[lane * kBucketsPerLane + i] = off;
+    for (int i = 0; i < kBucketsPerThread; ++i) {
+      bucket[tid * kBucketsPerThread + i] = off;
       off += c[i];
     }
   }
   __syncthreads();
 
-  for (int s = lane; s < N; s += kPlanLanes) {
+  for (int s = tid; s < N; s += kPlanThreads) {
     int n, L;
     const int nt = seq(s, n, L);
     if (nt == 0) continue;
@@ -384,13 +424,13 @@ __global__ void __launch_bounds__(kPlanLanes) plan_kernel(const PlanParams p) {
       if (np > 1) pr += np * rows_t * Hkv;
     }
   }
-  for (int i = lane; i < units_v; i += kPlanLanes) {
+  for (int i = tid; i < units_v; i += kPlanThreads) {
     const int tv = i / npv;
     const int k = (i - tv * npv) * Pv;
     const int slot = atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
     p.buf.units[slot] = make_int4(N, tv, k, -1);
   }
-  if (lane == 0) {
+  if (tid == 0) {
     p.buf.tile_base[N] = total_tiles;
     p.buf.hdr[kHdrUnits] = units_total;
     p.buf.hdr[kHdrQueue] = 0;
@@ -469,7 +509,8 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
 }  // namespace
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanLanes), 0, stream, p);
+  if (p.num_seqs > 128) hipLaunchKernelGGL(plan_kernel<256>, dim3(1), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(plan_kernel<64>, dim3(1), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
