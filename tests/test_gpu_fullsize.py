@@ -52,3 +52,32 @@ def test_full_size_sampled(name):
     rows = np.concatenate([np.arange(st.query_start_loc[s], st.query_start_loc[s + 1]) for s in seqs])
     got = out_f64(out)
     check_close(got[rows], ref[rows], BF16, f"full {name} seqs {seqs}")
+
+
+def test_full_size_prefix_pass_sampled():
+    """The prefix-sharing batch at full size through paged_attention_forward_prefix (the configuration
+    bench.py --prefix-pass times): all 256 sequences share 128 blocks; sampled sequences against the oracle,
+    and the whole output against the ordinary entry point's."""
+    pkv.set_tuning(0, 0, 0)
+    w = make_config("prefix", "full")
+    st = w.steps[0]
+    log(f"full prefix, shared-prefix pass: {w.description}")
+    dw = DeviceWorkload(w)
+    out_plain = dw.run_step(0).clone()  # writes this step's K/V, then the ordinary computation
+    s = dw.steps[0]
+    out = pkv.paged_attention_forward_prefix(s["q"], dw.k_pool, dw.v_pool, dw.block_tables, s["context_lens"],
+                                             s["query_start_loc"], 0, w.num_seqs,
+                                             w.shared_prefix_blocks * w.block_size, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    L = st.context_lens
+    seqs = sorted(set([int(np.argmin(L)), int(np.argmax(L)), 0, w.num_seqs - 1]
+                      + rng.choice(w.num_seqs, 2, replace=False).tolist()))
+    k2, v2 = oracle.kv_write(w.k_pool, w.v_pool, st.k_new, st.v_new, st.slot_mapping)
+    ref = oracle.paged_attention(st.q, k2, v2, w.block_tables, st.context_lens, st.query_start_loc,
+                                 w.scale, w.dtype, seqs=seqs)
+    rows = np.concatenate([np.arange(st.query_start_loc[q], st.query_start_loc[q + 1]) for q in seqs])
+    check_close(out_f64(out)[rows], ref[rows], BF16, f"full prefix pass seqs {seqs}")
+    # every row: the two entry points differ only by float32 summation order and bf16 rounding
+    diff = (out.float() - out_plain.float()).abs()
+    assert float(diff.max()) <= 2e-2 and float(diff.mean()) <= 2e-3, (float(diff.max()), float(diff.mean()))
