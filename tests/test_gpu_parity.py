@@ -253,6 +253,32 @@ def test_layer_inside_block_pool(workload, layers, layer):
             assert int((big_k[:, other] != 0).sum()) == 0 and int((big_v[:, other] != 0).sum()) == 0
 
 
+def test_long_context_chunk_splits_automatically():
+    """A 384-token chunk over a long prior context (kv 2 heads, G 4: 1536 rows, six 256-row tiles, up to
+    12000 keys) plus two decodes: with default tuning the tall tiles take the wide partition (at least 4096
+    keys) and split, so split_reduce merges tall-tile partials; checked against the oracle, and the plan's
+    partition words are checked to show the split happened."""
+    w = build_workload(np.random.default_rng(31), name="longchunk", dtype=BF16, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, q_lens=[384, 1, 1],
+                       context_lens=[12000, 700, 5000])
+    log("long-context chunk, automatic split of tall tiles")
+    dw = DeviceWorkload(w)
+    st = dw.steps[0]
+    ws = torch.zeros(max(256, pkv.workspace_size(w.num_seqs, st["q"].shape[0], w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, st["q"].dtype, st["max_q_len"])),
+                     dtype=torch.uint8, device=st["q"].device)
+    pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], dw.k_pool, dw.v_pool)
+    out = pkv.paged_attention_forward(st["q"], dw.k_pool, dw.v_pool, dw.block_tables, st["context_lens"],
+                                      st["query_start_loc"], scale=w.scale, workspace=ws,
+                                      max_q_len=st["max_q_len"])
+    torch.cuda.synchronize()
+    hdr = ws[:64].cpu().numpy().view(np.int32)
+    wide_partition = int(hdr[5])
+    assert 4096 <= wide_partition < 12000, wide_partition  # the tall tiles were split
+    _, _, outs = _oracle_steps(w)
+    check_close(out_f64(out), outs[0], BF16, "long-context chunk")
+
+
 def test_empty_and_degenerate():
     """num_seqs == 0 and num_tokens == 0 are no-ops; q_len 0 sequences are skipped."""
     w = build_workload(np.random.default_rng(5), name="deg", dtype=BF16, num_q_heads=8, num_kv_heads=2,
