@@ -295,13 +295,28 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   }
   const int units_v = tiles_v * npv;
 
-  // Partitions of tile t of sequence s for partition lengths (P_, Pw_): own key range starts at *k0
-  // (after the prefix for members of the shared-prefix pass), *np_own partitions of *len keys over it;
-  // returns all partitions of the tile including the prefix ones.
-  auto tile_parts = [&](int s, int n, int L, int rows, int t, int P_, int Pw_, const FastDiv& dp,
-                        const FastDiv& dw, int& len, int& k0, int& np_own) -> int {
-    const int rows_t = min(RT, rows - t * RT);
-    const int km = geo.kmax(L, n, rows, t);
+  // Tile list: record (sequence, tile) of every tile once, so that the passes below run one thread per
+  // tile rather than one per sequence (a long chunk has many tiles).  The records are completed (first
+  // partial row, partitions) once P is known.
+  for (int s = tid; s < N; s += kPlanThreads) {
+    int n, L;
+    const int nt = seq(s, n, L);
+    const int tb = s < kSeqCache ? tbase[s] : p.buf.tile_base[s];
+    for (int t = 0; t < nt; ++t) p.buf.tile_rec[tb + t] = make_int4(s, t, -1, 0);
+  }
+  __syncthreads();  // (also a workgroup-scope fence: the records are visible to every thread)
+
+  // Partitions of tile record rec for partition lengths (P_, Pw_).  Its own key range starts at *k0
+  // (after the prefix for members of the shared-prefix pass) and has *np_own partitions of *len keys;
+  // returns all partitions of the tile including the prefix ones.  Also gives the tile's rows and kmax.
+  auto tile_parts = [&](const int4 rec, int P_, int Pw_, const FastDiv& dp, const FastDiv& dw, int& len, int& k0,
+                        int& np_own, int& rows_t, int& km) -> int {
+    int n, L;
+    const int s = rec.x, t = rec.y;
+    seq(s, n, L);
+    const int rows = n * G;
+    rows_t = min(RT, rows - t * RT);
+    km = geo.kmax(L, n, rows, t);
     const bool member = pref && s >= pb && s < pe;
     k0 = member ? ptok : 0;
     len = rows_t > kSmallTileRows ? Pw_ : P_;
@@ -315,16 +330,11 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const int Pw = wide_len(P);
     const FastDiv divp(P), divw(Pw);
     int units = 0, prows = 0;
-    for (int s = tid; s < N; s += kPlanThreads) {
-      int n, L;
-      const int nt = seq(s, n, L);
-      const int rows = n * G;
-      for (int t = 0; t < nt; ++t) {
-        int len, k0, np_own;
-        const int np = tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
-        units = min(units + np_own, kSat);
-        if (np > 1) prows = min(prows + min(np * min(RT, rows - t * RT), kSat) * Hkv, kSat);
-      }
+    for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
+      int len, k0, np_own, rows_t, km;
+      const int np = tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km);
+      units = min(units + np_own, kSat);
+      if (np > 1) prows = min(prows + min(np * rows_t, kSat) * Hkv, kSat);
     }
     units_total = block_sum<kPlanWaves>(units, red) + units_v;
     const int prows_total = block_sum<kPlanWaves>(prows, red);
@@ -334,26 +344,22 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
 
   const int Pw = wide_len(P);
   const FastDiv divp(P), divw(Pw);
-  // First partial row of every sequence's split tiles, in sequence order.
+  // Complete the tile records: first partial row of every split tile, in tile (= sequence) order.
   {
     int run = 0;
-    for (int base = 0; base < N; base += kPlanThreads) {
-      const int s = base + tid;
-      int pr = 0;
-      if (s < N) {
-        int n, L;
-        const int nt = seq(s, n, L);
-        const int rows = n * G;
-        for (int t = 0; t < nt; ++t) {
-          int len, k0, np_own;
-          const int np = tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
-          if (np > 1) pr += np * min(RT, rows - t * RT) * Hkv;
-        }
+    for (int base = 0; base < total_tiles; base += kPlanThreads) {
+      const int tau = base + tid;
+      int pr = 0, np = 0;
+      int4 rec = make_int4(0, 0, -1, 0);
+      if (tau < total_tiles) {
+        rec = p.buf.tile_rec[tau];
+        int len, k0, np_own, rows_t, km;
+        np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km);
+        if (np > 1) pr = np * rows_t * Hkv;
       }
       int sum;
       const int first = run + block_exclusive_scan<kPlanWaves>(pr, &sum, red);
-      if (s < kSeqCache) seqc[s].w = first;
-      else if (s < N) p.buf.seq_units[s] = first;
+      if (tau < total_tiles) p.buf.tile_rec[tau] = make_int4(rec.x, rec.y, np > 1 ? first : -1, np);
       run += sum;
     }
   }
@@ -362,16 +368,10 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
 #pragma unroll
   for (int i = 0; i < kBucketsPerThread; ++i) bucket[tid * kBucketsPerThread + i] = 0;
   __syncthreads();
-  for (int s = tid; s < N; s += kPlanThreads) {
-    int n, L;
-    const int nt = seq(s, n, L);
-    const int rows = n * G;
-    for (int t = 0; t < nt; ++t) {
-      int len, k0, np_own;
-      tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
-      const int km = geo.kmax(L, n, rows, t);
-      for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len))], 1);
-    }
+  for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
+    int len, k0, np_own, rows_t, km;
+    tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km);
+    for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len))], 1);
   }
   for (int i = tid; i < units_v; i += kPlanThreads) {
     const int k = (i % npv) * Pv;
@@ -396,32 +396,23 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   }
   __syncthreads();
 
-  for (int s = tid; s < N; s += kPlanThreads) {
-    int n, L;
-    const int nt = seq(s, n, L);
-    if (nt == 0) continue;
-    const int rows = n * G;
-    int tb = s < kSeqCache ? tbase[s] : p.buf.tile_base[s];
-    int pr = s < kSeqCache ? seqc[s].w : p.buf.seq_units[s];
-    for (int t = 0; t < nt; ++t) {
-      const int km = geo.kmax(L, n, rows, t);
-      const int rows_t = min(RT, rows - t * RT);
-      int len, k0, np_own;
-      const int np = tile_parts(s, n, L, rows, t, P, Pw, divp, divw, len, k0, np_own);
-      p.buf.tile_rec[tb] = make_int4(s, t, np > 1 ? pr : -1, np);
-      ++tb;
-      for (int pp = 0; pp < np_own; ++pp) {
-        const int kb = k0 + pp * len;
-        const int slot = atomicAdd(&bucket[sort_bucket(min(km - kb, len))], 1);
-        p.buf.units[slot] = make_int4(s, t, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
-      }
-      if (np > np_own) {
-        // member of the shared-prefix pass: its query tokens find their prefix partial rows here
-        const int q_lo = qsl[s];
-        const int4 info = make_int4(s, pr + np_own * rows_t * Hkv, rows_t, q_lo);
-        for (int i = 0; i < n; ++i) p.buf.tok_info[q_lo - vq0 + i] = info;
-      }
-      if (np > 1) pr += np * rows_t * Hkv;
+  for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
+    const int4 rec = p.buf.tile_rec[tau];
+    int len, k0, np_own, rows_t, km;
+    const int np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km);
+    const int pr = rec.z;
+    for (int pp = 0; pp < np_own; ++pp) {
+      const int kb = k0 + pp * len;
+      const int slot = atomicAdd(&bucket[sort_bucket(min(km - kb, len))], 1);
+      p.buf.units[slot] = make_int4(rec.x, rec.y, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
+    }
+    if (np > np_own) {
+      // member of the shared-prefix pass (one tile): its query tokens find their prefix partial rows here
+      const int s = rec.x;
+      const int q_lo = qsl[s];
+      const int n = rows_t / G;
+      const int4 info = make_int4(s, pr + np_own * rows_t * Hkv, rows_t, q_lo);
+      for (int i = 0; i < n; ++i) p.buf.tok_info[q_lo - vq0 + i] = info;
     }
   }
   for (int i = tid; i < units_v; i += kPlanThreads) {
