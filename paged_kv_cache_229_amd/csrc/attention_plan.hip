@@ -157,7 +157,6 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   constexpr int kBucketsPerThread = kSortBuckets / THREADS;
   __shared__ int bucket[kSortBuckets];
   __shared__ int4 seqc[kSeqCache];  // (n, L, tiles, first partial row) per sequence
-  __shared__ int tbase[kSeqCache];  // first tile record per sequence
   const int tid = threadIdx.x;
   __shared__ int red[kPlanWaves];
   const int N = p.num_seqs;
@@ -229,11 +228,15 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const int nt = s < N ? seq(s, n, L) : 0;
     int sum;
     const int first = total_tiles + block_exclusive_scan<kPlanWaves>(nt, &sum, red);
-    if (s < kSeqCache) tbase[s] = first;
-    if (s < N) p.buf.tile_base[s] = first;
+    // Tile list: record (sequence, tile) of every tile once, so that the passes below run one thread per
+    // tile rather than one per sequence (a long chunk has many tiles).  The records are completed (first
+    // partial row, partitions) once P is known.
+    if (first + nt <= p.tile_cap)
+      for (int t = 0; t < nt; ++t) p.buf.tile_rec[first + t] = make_int4(s, t, -1, 0);
     total_tiles += sum;
     if (total_tiles > p.tile_cap) break;
   }
+  __syncthreads();  // (also a workgroup-scope fence: the tile records are visible to every thread)
 
   if (total_tiles > p.tile_cap) {  // inconsistent metadata: do nothing
     if (tid == 0) {
@@ -294,17 +297,6 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     if (!pref) vn = tiles_v = npv = 0;
   }
   const int units_v = tiles_v * npv;
-
-  // Tile list: record (sequence, tile) of every tile once, so that the passes below run one thread per
-  // tile rather than one per sequence (a long chunk has many tiles).  The records are completed (first
-  // partial row, partitions) once P is known.
-  for (int s = tid; s < N; s += kPlanThreads) {
-    int n, L;
-    const int nt = seq(s, n, L);
-    const int tb = s < kSeqCache ? tbase[s] : p.buf.tile_base[s];
-    for (int t = 0; t < nt; ++t) p.buf.tile_rec[tb + t] = make_int4(s, t, -1, 0);
-  }
-  __syncthreads();  // (also a workgroup-scope fence: the records are visible to every thread)
 
   // Partitions of tile record rec for partition lengths (P_, Pw_).  Its own key range starts at *k0
   // (after the prefix for members of the shared-prefix pass) and has *np_own partitions of *len keys;
@@ -422,7 +414,6 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     p.buf.units[slot] = make_int4(N, tv, k, -1);
   }
   if (tid == 0) {
-    p.buf.tile_base[N] = total_tiles;
     p.buf.hdr[kHdrUnits] = units_total;
     p.buf.hdr[kHdrQueue] = 0;
     p.buf.hdr[kHdrPartition] = P;

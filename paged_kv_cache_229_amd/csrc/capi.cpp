@@ -82,7 +82,7 @@ int check_pool(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_
 }
 
 struct WsLayout {
-  size_t hdr, seq_tiles, seq_units, tile_base, tile_rec, units, part_ml, part_acc, tok_info, total;
+  size_t hdr, seq_tiles, tile_rec, units, part_ml, part_acc, tok_info, total;
   int rows_per_tile;
   int64_t tile_cap, unit_cap;
 };
@@ -110,10 +110,6 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   off = round256(off + 16 * sizeof(int));
   w.seq_tiles = off;
   off = round256(off + static_cast<size_t>(num_seqs) * sizeof(int));
-  w.seq_units = off;
-  off = round256(off + static_cast<size_t>(num_seqs) * sizeof(int));
-  w.tile_base = off;
-  off = round256(off + static_cast<size_t>(num_seqs + 1) * sizeof(int));
   w.tile_rec = off;
   off = round256(off + static_cast<size_t>(w.tile_cap) * 4 * sizeof(int));
   w.units = off;
@@ -304,8 +300,6 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   pkv::PlanBuffers b{};
   b.hdr = reinterpret_cast<int*>(ws + w.hdr);
   b.seq_tiles = reinterpret_cast<int*>(ws + w.seq_tiles);
-  b.seq_units = reinterpret_cast<int*>(ws + w.seq_units);
-  b.tile_base = reinterpret_cast<int*>(ws + w.tile_base);
   b.tile_rec = reinterpret_cast<int4*>(ws + w.tile_rec);
   b.units = reinterpret_cast<int4*>(ws + w.units);
   b.part_ml = reinterpret_cast<float2*>(ws + w.part_ml);

@@ -52,8 +52,6 @@ constexpr int kWidePartitionMin = 4096;
 struct PlanBuffers {
   int* hdr;         // [16]
   int* seq_tiles;   // [num_seqs]  scratch
-  int* seq_units;   // [num_seqs]  scratch
-  int* tile_base;   // [num_seqs + 1] first tile record of each sequence
   int4* tile_rec;   // [tile_cap]  {sequence, tile, first partial row or -1, number of partitions}
   int4* units;      // [unit_cap]  {sequence, tile, first key of the partition, first partial row or -1 if unsplit}
   float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
