@@ -1,7 +1,7 @@
 // Device-side work plan and split-context reduction for paged attention.
 //
 // The host never reads context_lens or query_start_loc (that would need a device-to-host sync), so the
-// decomposition into work is made here, on the device, by one wave:
+// decomposition into work is made here, on the device, by one workgroup (one wave up to 128 sequences):
 //
 //   unit = (sequence s, row tile t, context partition p), processed once per kv head.
 //
@@ -10,11 +10,12 @@
 // tile t covers rows [t*RT, min(rows, (t+1)*RT)); its last token sees keys [0, kmax).  A tile whose kmax
 // exceeds its partition length is split into ceil(kmax / length) partitions.  Tiles of at most
 // kSmallTileRows rows (decode-like work) use P, picked so the whole call has about `target_items`
-// (unit, kv head) items, enough to fill 256 compute units several times over; taller tiles (long query
-// chunks) use max(P, kWidePartitionMin).  P is then lengthened until the split tiles' partial rows fit
-// the workspace.  Units are listed longest
-// first (counting sort on their 64-key stage count) so that the attention kernel's static, snake-ordered
-// assignment of items to workgroups stays balanced.
+// (unit, kv head) items, enough to fill 256 compute units several times over, but no shorter than
+// kSoftMinPartition keys while the call keeps two items per workgroup of the persistent grid; taller tiles
+// (long query chunks) use max(P, kWidePartitionMin).  P is then lengthened until the split tiles' partial
+// rows fit the workspace.  Units are listed longest first (counting sort on their 64-key stage count), the
+// order in which the attention kernel's workgroups claim them from one queue, so that the short ones fill
+// the end.
 //
 // Each partition of a split tile leaves (acc, m, l) per row; split_reduce_kernel merges them:
 //     M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
@@ -252,7 +253,8 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   }
 
   // Partition length of small tiles: about target_items items in all, a multiple of the stage, at least
-  // kMinPartition, and never longer than needed for the longest context.  Taller tiles use Pw >= P.
+  // kMinPartition (kSoftMinPartition while that leaves min_items items), and never longer than needed for
+  // the longest context.  Taller tiles use Pw >= P.
   const int pmax = max(kMinPartition, (max_kmax + kStageKeys - 1) / kStageKeys * kStageKeys);
   int P;
   if (p.forced_partition > 0) {
@@ -262,6 +264,10 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const long long want = (items + p.target_items - 1) / p.target_items;
     P = static_cast<int>(min(static_cast<long long>(pmax), (want + kStageKeys - 1) / kStageKeys * kStageKeys));
     P = max(P, kMinPartition);
+    if (p.min_items > 0) {
+      const long long soft = min(static_cast<long long>(kSoftMinPartition), items / p.min_items / kStageKeys * kStageKeys);
+      P = max(P, static_cast<int>(min(soft, static_cast<long long>(pmax))));
+    }
   }
   auto wide_len = [&](int P_) { return p.forced_partition > 0 ? P_ : min(max(P_, kWidePartitionMin), pmax); };
 

@@ -320,6 +320,8 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   int items = g_target_items > 0 ? g_target_items : pkv::kDefaultItems;
   if (items > pkv::kMaxItems) items = pkv::kMaxItems;
   pp.target_items = items;
+  const int64_t grid_wgs = static_cast<int64_t>(num_cus()) * pkv::attention_bf16_wgs_per_cu(head_dim, tile_kind);
+  pp.min_items = g_target_items > 0 ? 0 : static_cast<int>(2 * grid_wgs);
   pp.forced_partition = g_partition_keys;
   pp.unit_cap = static_cast<int>(w.unit_cap);
   pp.tile_cap = static_cast<int>(w.tile_cap);
@@ -329,7 +331,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
 
   hipError_t e = pkv::launch_plan(pp, st);
   if (e != hipSuccess) return hip_fail("plan launch", e);
-  int64_t grid = static_cast<int64_t>(num_cus()) * pkv::attention_bf16_wgs_per_cu(head_dim, tile_kind);
+  int64_t grid = grid_wgs;
   const int64_t max_items = w.unit_cap * num_kv_heads;
   if (grid > max_items) grid = max_items;
   if (timed) hipEventRecord(g_ev_start, st);

@@ -21,6 +21,10 @@ constexpr int kMaxTileRows = tile_rows_of(2);
 constexpr int kMaxItems = 4096;
 constexpr int kDefaultItems = 1024;
 constexpr int kMinPartition = 256;
+// With the automatic item target, partitions are lengthened up to this many keys as long as the call
+// keeps PlanParams::min_items items: every item costs a pipeline fill and an epilogue, so fewer, longer
+// items are faster while there are enough of them to balance the grid.
+constexpr int kSoftMinPartition = 2048;
 
 // Workspace header words.
 enum HeaderWord {
@@ -86,6 +90,7 @@ struct PlanParams {
   int rows_per_tile;
   int max_context;    // max_blocks_per_seq * block_size: longer contexts are rejected on the device
   int target_items;
+  int min_items;      // 0, or the item count that partitions may not be lengthened below (see kSoftMinPartition)
   int forced_partition;
   int unit_cap;
   int tile_cap;

@@ -279,6 +279,31 @@ def test_long_context_chunk_splits_automatically():
     check_close(out_f64(out), outs[0], BF16, "long-context chunk")
 
 
+def test_single_long_decode_keeps_the_grid_busy():
+    """One sequence decoding over 32768 keys (GQA 32/8): with default tuning the context is still split into
+    enough partitions for two items per workgroup of the persistent grid (the planner's soft minimum
+    partition length gives way), and the merged result matches the oracle."""
+    w = build_workload(np.random.default_rng(37), name="onelong", dtype=BF16, num_q_heads=32,
+                       num_kv_heads=8, head_dim=128, block_size=16, q_lens=[1], context_lens=[32768])
+    log("single long decode, automatic partitions")
+    dw = DeviceWorkload(w)
+    st = dw.steps[0]
+    ws = torch.zeros(max(256, pkv.workspace_size(w.num_seqs, st["q"].shape[0], w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, st["q"].dtype, st["max_q_len"])),
+                     dtype=torch.uint8, device=st["q"].device)
+    pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], dw.k_pool, dw.v_pool)
+    out = pkv.paged_attention_forward(st["q"], dw.k_pool, dw.v_pool, dw.block_tables, st["context_lens"],
+                                      st["query_start_loc"], scale=w.scale, workspace=ws,
+                                      max_q_len=st["max_q_len"])
+    torch.cuda.synchronize()
+    hdr = ws[:64].cpu().numpy().view(np.int32)
+    items = int(hdr[0]) * w.num_kv_heads
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert items >= 2 * cus, (items, cus)
+    _, _, outs = _oracle_steps(w)
+    check_close(out_f64(out), outs[0], BF16, "single long decode")
+
+
 def test_empty_and_degenerate():
     """num_seqs == 0 and num_tokens == 0 are no-ops; q_len 0 sequences are skipped."""
     w = build_workload(np.random.default_rng(5), name="deg", dtype=BF16, num_q_heads=8, num_kv_heads=2,
