@@ -166,6 +166,9 @@ def main() -> None:
     ap.add_argument("--layers", type=int, default=1,
                     help="pool layout [num_blocks, layers, block_size, H_kv, D] (layer inside the block), "
                          "attending the last layer through block_stride; 1 = per-layer pool")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay captured HIP graphs of the step instead of launching each step from the host "
+                         "(slower on ROCm 7: graph dispatch adds more than the host launches it saves)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -260,15 +263,47 @@ def main() -> None:
 
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    # --graph: one HIP graph per pool copy (the same kernels as an eager step), captured once and replayed
+    # back to back, as a serving loop replays its captured decode step.  Default: every step launched from
+    # the host.
+    graphs = []
+    if args.graph:
+        try:
+            for i in range(min(args.steps, len(copies))):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(args.warmup + i)
+                graphs.append(g)
+            for g in graphs:  # the first replay of each graph also uploads it
+                g.replay()
+            torch.cuda.synchronize()
+        except Exception as exc:  # noqa: BLE001 - any capture failure falls back to eager launches
+            pkv.set_profile_events(None, None)
+            print(f"[bench] graph capture unavailable ({exc}); timing eager launches", file=sys.stderr, flush=True)
+            graphs = []
+    launch = "hip_graph" if graphs else "eager"
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        pkv.set_profile_events(*pairs[i])
-        step(args.warmup + i)
-    pkv.set_profile_events(None, None)
+    if graphs:
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+    else:
+        for i in range(args.steps):
+            pkv.set_profile_events(*pairs[i])
+            step(args.warmup + i)
+        pkv.set_profile_events(None, None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if graphs:
+        # Events recorded by graph nodes cannot be timed, so the attention kernel's duration comes from the
+        # same K steps launched eagerly right after the timed replays, with HIP events on the launch stream.
+        for i in range(args.steps):
+            pkv.set_profile_events(*pairs[i])
+            step(args.warmup + i)
+        pkv.set_profile_events(None, None)
+        torch.cuda.synchronize()
     kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    del graphs
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
@@ -297,7 +332,7 @@ def main() -> None:
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "pool_copies": len(copies),
                    "pool_layout": "per_layer" if args.layers == 1 else f"layer_in_block x{args.layers}",
-                   "shared_prefix_pass": bool(prefix_tokens)},
+                   "shared_prefix_pass": bool(prefix_tokens), "launch": launch},
         "tokens_per_s": round(work["total_q"] / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attention_kernel_ms": {"mean": round(k_avg, 5), "p10": round(float(np.percentile(kernel_ms, 10)), 5),
