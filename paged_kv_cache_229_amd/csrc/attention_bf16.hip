@@ -16,7 +16,7 @@
 //    rows of an item are (query token, head of g's group) pairs, so all G heads sharing kv head g read
 //    each K/V byte once.
 //  * K/V stream HBM -> LDS with global_load_lds (no register staging) into a 4-deep ring of 64-key
-//    stages: while one stage is consumed, up to three are in flight.  Each wave fetches 16 keys of a
+//    stages: while one stage is consumed, up to three are in flight.  Each wave fetches 8 keys of a
 //    stage, one uniform physical block per wave-wide load (block_size >= keys per load), each load
 //    instruction covering whole 256-byte (D=128) rows.  Block-table entries come through scalar loads
 //    issued a stage ahead, so the data loads never wait on a lookup.

@@ -11,8 +11,8 @@ namespace pkv {
 constexpr int kStageKeys = 64;
 constexpr int kThreads = 256;
 // Row-tile kinds of the bf16 attention.  Kind 1: 128-row tiles, 8 waves of 16 rows (two waves per SIMD),
-// for rows-poor batches (decode, speculative decode).  Kind 2: 256-row tiles, 4 waves of 64 rows (one
-// wave per SIMD, 32 x 32 MFMA tiles), for long query chunks.
+// for rows-poor batches (decode, speculative decode).  Kind 2: 256-row tiles, 8 waves of 32 rows (two
+// waves per SIMD, 32 x 32 MFMA tiles), for long query chunks.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int tile_rows_of(int kind) { return kind == 1 ? 128 : 256; }
