@@ -457,41 +457,42 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
   const int RT = p.rows_per_tile;
   const int row0 = tile * RT;
   const int rows_here = min(RT, n * G - row0);
-  const int rl = blockIdx.z * RPW + threadIdx.x / D4;
-  if (rl >= rows_here) return;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const int d0 = (threadIdx.x % D4) * 4;
   const int64_t part_stride = static_cast<int64_t>(rows_here) * p.num_kv_heads;
-  const int64_t row_base = pb0 + static_cast<int64_t>(g) * rows_here + rl;
-  float M = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  // Workgroup z merges row groups z, z + gridDim.z, ... of RPW rows each.
+  for (int rl = blockIdx.z * RPW + threadIdx.x / D4; rl < rows_here; rl += gridDim.z * RPW) {
+    const int64_t row_base = pb0 + static_cast<int64_t>(g) * rows_here + rl;
+    float M = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll 4
-  for (int pp = 0; pp < np; ++pp) {
-    const int64_t prow = row_base + pp * part_stride;
-    const float2 ml = p.buf.part_ml[prow];
-    const float4 a = *reinterpret_cast<const float4*>(p.buf.part_acc + prow * D + d0);
-    const float mnew = fmaxf(M, ml.x);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float s_old = __builtin_amdgcn_exp2f(M - mref);
-    const float s_new = __builtin_amdgcn_exp2f(ml.x - mref);
-    den = den * s_old + ml.y * s_new;
-    a0 = a0 * s_old + a.x * s_new;
-    a1 = a1 * s_old + a.y * s_new;
-    a2 = a2 * s_old + a.z * s_new;
-    a3 = a3 * s_old + a.w * s_new;
-    M = mnew;
+    for (int pp = 0; pp < np; ++pp) {
+      const int64_t prow = row_base + pp * part_stride;
+      const float2 ml = p.buf.part_ml[prow];
+      const float4 a = *reinterpret_cast<const float4*>(p.buf.part_acc + prow * D + d0);
+      const float mnew = fmaxf(M, ml.x);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float s_old = __builtin_amdgcn_exp2f(M - mref);
+      const float s_new = __builtin_amdgcn_exp2f(ml.x - mref);
+      den = den * s_old + ml.y * s_new;
+      a0 = a0 * s_old + a.x * s_new;
+      a1 = a1 * s_old + a.y * s_new;
+      a2 = a2 * s_old + a.z * s_new;
+      a3 = a3 * s_old + a.w * s_new;
+      M = mnew;
+    }
+    const float inv = 1.f / den;
+    const int r = row0 + rl;
+    const int i = r / G;
+    const int hh = r - i * G;
+    __bf16* o = static_cast<__bf16*>(p.out) +
+                ((static_cast<int64_t>(q0 + i) * p.num_q_heads + g * G + hh) * D + d0);
+    bf16x4 v;
+    v[0] = static_cast<__bf16>(a0 * inv);
+    v[1] = static_cast<__bf16>(a1 * inv);
+    v[2] = static_cast<__bf16>(a2 * inv);
+    v[3] = static_cast<__bf16>(a3 * inv);
+    *reinterpret_cast<bf16x4*>(o) = v;
   }
-  const float inv = 1.f / den;
-  const int r = row0 + rl;
-  const int i = r / G;
-  const int hh = r - i * G;
-  __bf16* o = static_cast<__bf16*>(p.out) +
-              ((static_cast<int64_t>(q0 + i) * p.num_q_heads + g * G + hh) * D + d0);
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v;
-  v[0] = static_cast<__bf16>(a0 * inv);
-  v[1] = static_cast<__bf16>(a1 * inv);
-  v[2] = static_cast<__bf16>(a2 * inv);
-  v[3] = static_cast<__bf16>(a3 * inv);
-  *reinterpret_cast<bf16x4*>(o) = v;
 }
 
 }  // namespace
@@ -504,9 +505,11 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
 
 hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream) {
   if (tile_cap <= 0) return hipSuccess;
+  // One workgroup per (tile, kv head, quarter of the tile's row groups): most tiles are not split and their
+  // workgroups return at once, so the grid is kept small rather than one workgroup per row group.
   const int rows_per_wg = kThreads / (head_dim / 4);
-  const dim3 grid(static_cast<unsigned>(tile_cap), static_cast<unsigned>(p.num_kv_heads),
-                  static_cast<unsigned>((kMaxTileRows + rows_per_wg - 1) / rows_per_wg));
+  const int z = (p.rows_per_tile + 4 * rows_per_wg - 1) / (4 * rows_per_wg);
+  const dim3 grid(static_cast<unsigned>(tile_cap), static_cast<unsigned>(p.num_kv_heads), static_cast<unsigned>(z));
   if (head_dim == 128) {
     hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(kThreads), 0, stream, p);
   } else {
