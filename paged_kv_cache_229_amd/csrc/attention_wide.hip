@@ -32,6 +32,16 @@ namespace {
 // 2 = four waves of 64 rows (one per SIMD).
 constexpr int kWideHalves = 1;
 
+// 16-byte-chunk swizzle of LDS row `key` for this kernel's reads.  For D = 128 (16 chunks per row) the two
+// low bits of the key pick the upper two bits of the chunk mask and the next two bits the lower two: the
+// four keys that one half-wave's V transpose read covers (4 chunks each) then land on 16 distinct chunks,
+// and K's 16-byte reads (16 keys per 16 lanes, one chunk each) stay on distinct chunks too.  The plain
+// key-as-mask swizzle puts those four keys on the same four chunks (a 4-way bank conflict).
+template <int D>
+__device__ inline int wide_swizzle(int key) {
+  return D == 128 ? (((key & 3) << 2) | ((key >> 2) & 3)) : ((key >> 1) & 7);
+}
+
 template <int D, int NH>
 struct WideGeo {
   static constexpr int CPK = D / 8;             // 16-byte chunks per K/V row of one head
@@ -102,7 +112,7 @@ attn_wide_kernel(const AttnParams p) {
   // groups (+16, +32) are constant offsets: the swizzle depends on the key modulo 16 only.
   int kof[T::KS];
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) kof[ks] = l32 * T::ROWB + (((2 * ks + hf) ^ k_swizzle<D>(l32)) << 4);
+  for (int ks = 0; ks < T::KS; ++ks) kof[ks] = l32 * T::ROWB + (((2 * ks + hf) ^ wide_swizzle<D>(l32)) << 4);
   int vof[T::DT][2];
   {
     const int gi = lane & 15, gq = (lane >> 4) & 1;
@@ -112,7 +122,7 @@ attn_wide_kernel(const AttnParams p) {
       for (int e8 = 0; e8 < 2; ++e8) {
         const int key = 4 * hf + (gi >> 2) + 8 * e8;
         vof[dt][e8] = T::TILEB + key * T::ROWB + (gi & 1) * 8 +
-                      (((4 * dt + 2 * gq + ((gi & 3) >> 1)) ^ k_swizzle<D>(key)) << 4);
+                      (((4 * dt + 2 * gq + ((gi & 3) >> 1)) ^ wide_swizzle<D>(key)) << 4);
       }
   }
 
@@ -182,7 +192,7 @@ attn_wide_kernel(const AttnParams p) {
         const int key_local = T::KPW * wave + T::KPL * i + lane / T::CPK;
         const int kk = min(key0 + T::KPL * i + lane / T::CPK, ke - 1);
         const int ph = min(max(phys[i], 0), last_block);
-        const int c = (lane % T::CPK) ^ k_swizzle<D>(key_local);
+        const int c = (lane % T::CPK) ^ wide_swizzle<D>(key_local);
         const int64_t e = static_cast<int64_t>(ph) * p.block_stride +
                           (static_cast<int64_t>(kk & bs_mask) * Hkv + g) * D + c * 8;
         const unsigned dk =
