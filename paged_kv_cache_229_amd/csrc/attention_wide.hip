@@ -125,6 +125,11 @@ attn_wide_kernel(const AttnParams p) {
       }
   }
 
+  // Waves w and w + 4 share a SIMD.  Giving the lower one a higher issue priority lets its QK MFMAs run
+  // first after each stage barrier, so that its softmax overlaps the partner's QK and its PV the partner's
+  // softmax, instead of both waves reaching their vector phases together.
+  if (T::NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(1);
+
   // The next item is claimed while the current one finishes, so the atomic's latency hides behind the
   // epilogue.
   int next_item = 0;
