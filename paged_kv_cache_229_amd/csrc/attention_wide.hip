@@ -103,6 +103,7 @@ attn_wide_kernel(const AttnParams p) {
   const __bf16* const qg = static_cast<const __bf16*>(p.q);
   __bf16* const og = static_cast<__bf16*>(p.out);
   const float sl2 = p.scale_log2;
+  const float inv_sl2 = 1.f / sl2;
   const unsigned lds_ring = static_cast<unsigned>(reinterpret_cast<size_t>((LDS_AS unsigned char*)smem));
 
   // Lane offsets of the fragment reads inside a stage slot.  K (A operand of S^T): key l32, 16-byte chunk
@@ -221,9 +222,8 @@ attn_wide_kernel(const AttnParams p) {
     if (nst > 2) fetch_table(2, tb2);
     if (nst > 3) fetch_table(3, tbn);
 
-    // Query fragments of both halves (B operand: Q[row][16ks + 8hf + 0..7]), multiplied by scale * log2(e)
-    // and rounded to bf16 once per item, so that the QK MFMAs give scores in log2 units; and each lane
-    // row's last visible key (-1 for padding rows).
+    // Query fragments of both halves (B operand: Q[row][16ks + 8hf + 0..7]) and each lane row's last
+    // visible key (-1 for padding rows).
     bf16x8 q[NH][T::KS];
     int lim[NH];
 #pragma unroll
@@ -234,11 +234,7 @@ attn_wide_kernel(const AttnParams p) {
         const int rh = r - ri * G;
         const __bf16* const qp = qg + ((static_cast<int64_t>(q0 + ri) * Hq + g * G + rh) * D + 8 * hf);
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-          const bf16x8 raw = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
-#pragma unroll
-          for (int t = 0; t < 8; ++t) q[h][ks][t] = static_cast<__bf16>(static_cast<float>(raw[t]) * sl2);
-        }
+        for (int ks = 0; ks < T::KS; ++ks) q[h][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
         lim[h] = min(L - n + ri, ke - 1);
       } else {
 #pragma unroll
@@ -254,20 +250,13 @@ attn_wide_kernel(const AttnParams p) {
     if (nst > 2) issue(2, tb2);
 
     f32x16 acc[NH][T::DT];
-    // Per lane row: reference maximum mw (log2 units; -inf until the row's first visible key), the growth
-    // of a chunk's maximum over it that forces a rescale (thw), and the lane's share of the row sum (lw).
-    // negm holds -mw (0 while mw is -inf) in all 16 registers: it is the C operand of each chunk's first
-    // QK MFMA, so the MFMAs return score - mw and the exponent needs no subtraction.  It changes only
-    // when the reference maximum moves.
-    f32x16 negm[NH];
-    float mw[NH], thw[NH], lw[NH];
+    float mw[NH], thw[NH], nmw[NH], lw[NH];  // reference max (log2), growth threshold (raw), -max, lane sum
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       mw[h] = -INFINITY;
       thw[h] = -INFINITY;
+      nmw[h] = 0.f;
       lw[h] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) negm[h][j] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
@@ -283,10 +272,14 @@ attn_wide_kernel(const AttnParams p) {
     auto chunk = [&](const unsigned char* slot, int c, int kc0) __attribute__((always_inline)) {
       f32x16 sc[NH];
 #pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[h][j] = 0.f;
+#pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(slot + kof[ks] + 32 * c * T::ROWB));
 #pragma unroll
-        for (int h = 0; h < NH; ++h) sc[h] = mfma32(kf, q[h][ks], ks == 0 ? negm[h] : sc[h]);
+        for (int h = 0; h < NH; ++h) sc[h] = mfma32(kf, q[h][ks], sc[h]);
       }
       // V^T operands of both 16-key steps, read before the softmax so their latency hides behind it.
       bf16x8 vf[T::DT][2];
@@ -323,20 +316,15 @@ attn_wide_kernel(const AttnParams p) {
       if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-          const float mref = mw[h] == -INFINITY ? 0.f : mw[h];  // the maximum negm[h] subtracts
-          const float mnew = fmaxf(mw[h], pair_max(x[h]) + mref);  // lanes l, l^32 share the row
+          const float mnew = fmaxf(mw[h], pair_max(x[h]) * sl2);  // lanes l, l^32 share the row
           if (mnew != -INFINITY) {
             const float alpha = __builtin_amdgcn_exp2f(mw[h] - mnew);
             lw[h] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < T::DT; ++dt) acc[h][dt] *= alpha;
-            const float shift = mnew - mref;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sv[h][j] -= shift;
             mw[h] = mnew;
-            thw[h] = kLazyRescale;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) negm[h][j] = -mnew;
+            nmw[h] = -mnew;
+            thw[h] = (mnew + kLazyRescale) * inv_sl2;
           }
         }
       }
@@ -345,7 +333,8 @@ attn_wide_kernel(const AttnParams p) {
         // P^T (B operand) of step s2: the lane's keys 16s2 + 8(t/4) + 4hf + t%4, t < 8.
         bf16x8 pf[2];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) pf[j >> 3][j & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[h][j]));
+        for (int j = 0; j < 16; ++j)
+          pf[j >> 3][j & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][j], sl2, nmw[h])));
 #pragma unroll
         for (int j2 = 0; j2 < 8; ++j2) {
           bf16x2 pr;
