@@ -119,15 +119,12 @@ def test_tile_kinds(name, partition, kind):
     check_close(out_f64(out), outs[0], BF16, f"{name} kind={kind} P={partition}")
 
 
-@pytest.mark.parametrize("kind", [1, 2])
-@pytest.mark.parametrize("dtype", [BF16, FP32])
+@pytest.mark.parametrize("dtype,kind", [(BF16, 1), (BF16, 2), (FP32, 0)])  # the float32 path has no row tiles
 @pytest.mark.parametrize("head_dim,block_size,hq,hkv", [(64, 8, 8, 2), (64, 32, 4, 4), (128, 64, 16, 1),
                                                          (128, 256, 6, 3)])
 def test_geometries(dtype, head_dim, block_size, hq, hkv, kind):
     """head_dim 64/128, block sizes 8..256, MHA/GQA/MQA, ragged lengths including 1 and exact blocks,
-    under both row-tile shapes."""
-    if dtype == FP32 and kind == 2:
-        pytest.skip("the float32 path has no row tiles")
+    under both bf16 row-tile shapes and on the float32 path."""
     pkv.set_tuning(0, 0, kind)
     rng = np.random.default_rng(head_dim * 1000 + block_size + hq)
     q_lens = [1, 3, 1, 17, 0, 5, 1]
