@@ -11,13 +11,18 @@
 //    rate of the 16 x 16 x 32 form on MI355X): eight waves of one half (two per SIMD), or four waves of
 //    two halves, where every K or V fragment read from LDS feeds both halves.
 //  * K/V arrive in LDS through the same 4-deep ring of 64-key stages as the 16-row kernel (each wave
-//    copies 16 keys of a stage; block-table entries through scalar loads a stage ahead).
+//    copies 64 / waves keys of a stage, 8 with eight waves; block-table entries through scalar loads a
+//    stage ahead), under this kernel's own chunk swizzle (wide_swizzle), which keeps its V transpose
+//    reads free of bank conflicts.
 //  * S^T = K Q^T: A = K (32 keys x 16 channels, one 16-byte read per lane), B = Q^T from registers.
 //    Lane l holds row l % 32 and keys 8i + 4(l/32) + [0, 4), i < 4, of each 32-key chunk, so the row's
 //    maximum and sum need one exchange of the wave halves.
 //  * O^T += V^T P^T in two 16-key steps; the lane's own probabilities are the B operand in the order
 //    16s + 8(t/4) + 4(l/32) + t%4, and two ds_read_b64_tr_b16 per step give V^T in that order.
-//  * Lazy online softmax as in the 16-row kernel (reference maximum moves only on growth beyond 2^8).
+//  * Lazy online softmax as in the 16-row kernel (reference maximum moves only on growth beyond 2^8);
+//    row sums add the bf16 probabilities pairwise with v_dot2_f32_bf16, i.e. the values the PV MFMAs use.
+//  * The two waves sharing a SIMD (w and w + 4) run at different issue priorities, so their matrix and
+//    vector phases stagger instead of coinciding after every stage barrier.
 //  * Tiles with few rows (decode-like units of a mixed batch) split the keys among the waves, whose states
 //    are merged through LDS; split partitions write (acc, m, l) for split_reduce_kernel.
 #include <type_traits>
