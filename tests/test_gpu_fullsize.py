@@ -10,7 +10,7 @@ import torch
 import oracle
 import paged_kv_cache_229_amd as pkv
 from gpu_util import DeviceWorkload, check_close, log, out_f64
-from workloads import BF16, make_config
+from workloads import BF16, make_config, subset_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +81,25 @@ def test_full_size_prefix_pass_sampled():
     # every row: the two entry points differ only by float32 summation order and bf16 rounding
     diff = (out.float() - out_plain.float()).abs()
     assert float(diff.max()) <= 2e-2 and float(diff.mean()) <= 2e-3, (float(diff.max()), float(diff.mean()))
+
+
+def test_full_size_prefill_chunks_sampled():
+    """The 8 prefill chunks of the mixed step alone, in the launch `bench.py --workload mixed --subset
+    prefill` times (512-token chunks over up to 2048 prior tokens, 256-row tiles, automatic plan): the
+    chunks with the shortest and the longest context against the oracle, every row."""
+    pkv.set_tuning(0, 0, 0)
+    full = make_config("mixed", "full")
+    keep = np.nonzero(np.diff(full.steps[0].query_start_loc) > 1)[0]
+    w = subset_workload(full, keep)
+    st = w.steps[0]
+    log(f"full prefill chunks: {w.num_seqs} sequences, contexts {st.context_lens.tolist()}")
+    dw = DeviceWorkload(w)
+    out = dw.run_step(0)
+    torch.cuda.synchronize()
+    L = st.context_lens
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L))})
+    k2, v2 = oracle.kv_write(w.k_pool, w.v_pool, st.k_new, st.v_new, st.slot_mapping)
+    ref = oracle.paged_attention(st.q, k2, v2, w.block_tables, st.context_lens, st.query_start_loc,
+                                 w.scale, w.dtype, seqs=seqs)
+    rows = np.concatenate([np.arange(st.query_start_loc[s], st.query_start_loc[s + 1]) for s in seqs])
+    check_close(out_f64(out)[rows], ref[rows], BF16, f"full prefill chunks seqs {seqs}")
