@@ -130,11 +130,11 @@ attn_bf16_kernel(const AttnParams p) {
     // the vector-memory counter.
     const int unit = item / Hkv;
     const int g = item - unit * Hkv;
-    const CONST_AS int* const urec = (const CONST_AS int*)p.buf.units + 4 * unit;
+    const CONST_AS int* const urec = (const CONST_AS int*)p.buf.units + 8 * unit;
     const int s = urec[0], tile = urec[1], kb = urec[2], pbase = urec[3];
-    const int q0 = ((const CONST_AS int*)p.query_start_loc)[s];
-    const int n = ((const CONST_AS int*)p.query_start_loc)[s + 1] - q0;
-    const int L = ((const CONST_AS int*)p.context_lens)[s];
+    const int q0 = urec[4];  // the sequence's first query token, query tokens and context, from the plan
+    const int n = urec[5];
+    const int L = urec[6];
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;

@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   constexpr int kPlanWaves = THREADS / 64;
   constexpr int kBucketsPerThread = kSortBuckets / THREADS;
   __shared__ int bucket[kSortBuckets];
-  __shared__ int4 seqc[kSeqCache];  // (n, L, tiles, first partial row) per sequence
+  __shared__ int4 seqc[kSeqCache];  // (n, L, tiles, first query token) per sequence
   const int tid = threadIdx.x;
   __shared__ int red[kPlanWaves];
   const int N = p.num_seqs;
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       for (int t = 0; t < nt; ++t) work = min(work + (geo.kmax(L, n, rows, t) + kStageKeys - 1) / kStageKeys, kSat);
       maxk = max(maxk, L);  // the last tile's last row sees all L keys
     }
-    if (s < kSeqCache) seqc[s] = make_int4(n, L, nt, 0);
+    if (s < kSeqCache) seqc[s] = make_int4(n, L, nt, lo);
     else p.buf.seq_tiles[s] = nt;
   }
   const long long total_work = static_cast<long long>(block_sum<kPlanWaves>(work, red)) * kStageKeys;
@@ -399,10 +399,19 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     int len, k0, np_own, rows_t, km;
     const int np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km);
     const int pr = rec.z;
+    int4 sq;  // the sequence's first query token, query tokens and context
+    if (rec.x < kSeqCache) {
+      const int4 c = seqc[rec.x];
+      sq = make_int4(c.w, c.x, c.y, 0);
+    } else {
+      const int lo = qsl[rec.x];
+      sq = make_int4(lo, qsl[rec.x + 1] - lo, ctx[rec.x], 0);
+    }
     for (int pp = 0; pp < np_own; ++pp) {
       const int kb = k0 + pp * len;
       const int slot = atomicAdd(&bucket[sort_bucket(min(km - kb, len))], 1);
-      p.buf.units[slot] = make_int4(rec.x, rec.y, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
+      p.buf.units[2 * slot] = make_int4(rec.x, rec.y, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
+      p.buf.units[2 * slot + 1] = sq;
     }
     if (np > np_own) {
       // member of the shared-prefix pass (one tile): its query tokens find their prefix partial rows here
@@ -417,7 +426,8 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const int tv = i / npv;
     const int k = (i - tv * npv) * Pv;
     const int slot = atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
-    p.buf.units[slot] = make_int4(N, tv, k, -1);
+    p.buf.units[2 * slot] = make_int4(N, tv, k, -1);
+    p.buf.units[2 * slot + 1] = make_int4(vq0, vn, ptok - 1 + vn, 0);
   }
   if (tid == 0) {
     p.buf.hdr[kHdrUnits] = units_total;

@@ -94,9 +94,6 @@ attn_wide_kernel(const AttnParams p) {
   const int P = p.buf.hdr[kHdrPartition];
   const int Pw = p.buf.hdr[kHdrPartitionWide];
   // Shared-prefix sequence (index num_seqs in the unit records; absent when it has no tokens).
-  const int pre_q0 = p.buf.hdr[kHdrPrefQ0];
-  const int pre_n = p.buf.hdr[kHdrPrefN];
-  const int pre_L = p.buf.hdr[kHdrPrefL];
   const int pre_keys = p.buf.hdr[kHdrPrefKeys];
   const int pre_table = p.buf.hdr[kHdrPrefTable];
   const int pre_P = p.buf.hdr[kHdrPrefPartition];
@@ -149,15 +146,17 @@ attn_wide_kernel(const AttnParams p) {
 
     const int unit = item / Hkv;
     const int g = item - unit * Hkv;
-    const int4 u = p.buf.units[unit];
-    const int s = u.x, tile = u.y, kb = u.z, pbase = u.w;
+    // Unit record through scalar loads: {sequence, tile, first key, first partial row} and the sequence's
+    // {first query token, query tokens, context}.
+    const CONST_AS int* const urec = (const CONST_AS int*)p.buf.units + 8 * unit;
+    const int s = urec[0], tile = urec[1], kb = urec[2], pbase = urec[3];
     // The shared-prefix sequence: its query tokens are the member sequences' and every prefix key is
-    // visible to each of them (context pre_L = prefix length - 1 + token count); its rows' results are
+    // visible to each of them (its context is prefix length - 1 + token count); its rows' results are
     // partial rows of the members' tiles.
     const bool pre = s == p.num_seqs;
-    const int q0 = pre ? pre_q0 : p.query_start_loc[s];
-    const int n = pre ? pre_n : p.query_start_loc[s + 1] - q0;
-    const int L = pre ? pre_L : p.context_lens[s];
+    const int q0 = urec[4];
+    const int n = urec[5];
+    const int L = urec[6];
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;

@@ -113,7 +113,7 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   w.tile_rec = off;
   off = round256(off + static_cast<size_t>(w.tile_cap) * 4 * sizeof(int));
   w.units = off;
-  off = round256(off + static_cast<size_t>(w.unit_cap) * 4 * sizeof(int));
+  off = round256(off + static_cast<size_t>(w.unit_cap) * 8 * sizeof(int));
   const size_t part_rows = pkv::kPartialRowCap;
   w.part_ml = off;
   off = round256(off + part_rows * 2 * sizeof(float));

@@ -57,7 +57,10 @@ struct PlanBuffers {
   int* hdr;         // [16]
   int* seq_tiles;   // [num_seqs]  scratch
   int4* tile_rec;   // [tile_cap]  {sequence, tile, first partial row or -1, number of partitions}
-  int4* units;      // [unit_cap]  {sequence, tile, first key of the partition, first partial row or -1 if unsplit}
+  // [unit_cap][2]: {sequence, tile, first key of the partition, first partial row or -1 if unsplit}, then the
+  // sequence's {first query token, query tokens, context length, 0}, so that an item needs no further
+  // dependent metadata load
+  int4* units;
   float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
   float* part_acc;  // [prow_cap * head_dim] unnormalised partial outputs
   // [total_q] for query tokens of the shared-prefix sequences: {sequence, first partial row of its
