@@ -107,6 +107,69 @@ class HipEvents:
         self.rt.hipEventDestroy(ctypes.c_void_p(ev))
 
 
+def prefill_view(dev, steps: int, warmup: int, copies: int) -> dict:
+    """The other half of the metric: the chunked-prefill step's 8 prefill chunks alone (512 tokens each over a
+    prior context U[0, 2048], the launch `--workload mixed --subset prefill` times), with the attention kernel
+    timed by the library's HIP events and priced against the dense bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_229_amd as pkv
+    from workloads import make_config, subset_workload
+
+    w = make_config("mixed", "full")
+    keep = np.nonzero(np.diff(w.steps[0].query_start_loc) > 1)[0]
+    w = subset_workload(w, keep)
+    w.description += f" [prefill sequences only: {len(keep)}]"
+    work = algorithmic_work(w)
+    st = w.steps[0]
+
+    def t(a, is_data=True):
+        if is_data and a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    k0, v0 = t(w.k_pool), t(w.v_pool)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(0, copies - 1))]
+    bt = t(w.block_tables, False)
+    q, kn, vn = t(st.q), t(st.k_new), t(st.v_new)
+    sm, cl, qsl = t(st.slot_mapping, False), t(st.context_lens, False), t(st.query_start_loc, False)
+    max_q = int(np.diff(st.query_start_loc).max())
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, pkv.workspace_size(w.num_seqs, q.shape[0], w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, q.dtype, max_q)), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        kp, vp = pools[i % len(pools)]
+        pkv.paged_kv_write(kn, vn, sm, kp, vp)
+        pkv.paged_attention_forward(q, kp, vp, bt, cl, qsl, scale=w.scale, out=out, workspace=ws,
+                                    max_q_len=max_q)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    for i in range(steps):
+        pkv.set_profile_events(*pairs[i])
+        step(warmup + i)
+    pkv.set_profile_events(None, None)
+    torch.cuda.synchronize()
+    kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    k_avg = float(np.mean(kernel_ms))
+    tflops = work["flops"] / (k_avg * 1e-3) / 1e12
+    return {"workload": w.description, "kernel": "attn_wide_kernel", "bound": "mfma",
+            "attention_kernel_ms": {"mean": round(k_avg, 5), "p10": round(float(np.percentile(kernel_ms, 10)), 5),
+                                    "p90": round(float(np.percentile(kernel_ms, 90)), 5)},
+            "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": work["flops"],
+            "traffic": recorded_traffic("mixed:prefill"),
+            "tokens_per_s": round(work["total_q"] / (k_avg * 1e-3), 1)}
+
+
 def cpu_baseline(w, work, budget_s: float) -> dict:
     """The oracle as it stands, on the host cores, over the workload's step (K/V write, then attention one
     sequence at a time), repeated until at least min(10 s, budget_s) of work and stopped mid-step once
@@ -177,6 +240,8 @@ def main() -> None:
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graphs of the step instead of launching each step from the host "
                          "(slower on ROCm 7: graph dispatch adds more than the host launches it saves)")
+    ap.add_argument("--no-prefill-view", action="store_true",
+                    help="skip the prefill half of the metric that a default (decode) run adds as prefill_view")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -362,6 +427,11 @@ def main() -> None:
                                    "flops_per_launch": work["flops"]})
     if work["prefill_flops"]:
         result["prefill_subset_flops"] = work["prefill_flops"]
+    if (args.workload == "decode" and args.subset == "all" and args.layers == 1 and not args.graph
+            and not args.no_prefill_view):
+        del copies, ws, out
+        torch.cuda.empty_cache()
+        result["prefill_view"] = prefill_view(dev, args.steps, args.warmup, args.copies)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, work, args.cpu_budget)
     print(json.dumps(result), flush=True)
