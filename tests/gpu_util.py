@@ -67,8 +67,16 @@ class DeviceWorkload:
                                            scale=self.w.scale, out=out, max_q_len=s["max_q_len"])
 
 
+# RMS of the error relative to the RMS of the oracle's output, for bf16 results.  At long context the
+# N(0,1) outputs are only ~0.01 in size, so the absolute bounds alone barely constrain a wrong kernel;
+# rounding the output to bf16 alone gives ~1.5e-3 and the bf16 probabilities in PV add little, so 1e-2
+# leaves a margin of about 4x while any dropped, repeated or misread key block shows far above it.
+RMS_REL_BF16 = 1e-2
+
+
 def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> dict:
-    """bf16: max-abs <= 2e-2 and mean-abs <= 2e-3; fp32: max-abs <= 1e-5 (against the fp64 oracle)."""
+    """bf16: max-abs <= 2e-2, mean-abs <= 2e-3 and RMS-relative <= RMS_REL_BF16; fp32: max-abs <= 1e-5
+    (against the fp64 oracle).  Every value must be finite."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
@@ -78,6 +86,7 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> dict
     log(f"{what}: {stats}")
     if dtype == BF16:
         assert stats["max_abs"] <= 2e-2 and stats["mean_abs"] <= 2e-3, (what, stats)
+        assert stats["rms_rel"] <= RMS_REL_BF16, (what, stats)
     else:
         assert stats["max_abs"] <= 1e-5, (what, stats)
     return stats

@@ -139,11 +139,18 @@ def test_geometries(dtype, head_dim, block_size, hq, hkv, kind):
     check_close(out_f64(out), outs[0], dtype, f"geo D{head_dim} bs{block_size} {hq}/{hkv} {dtype}")
 
 
-def test_paging_invariance_and_determinism():
+# (dtype, tile kind): both bf16 row-tile shapes and the float32 path (which has no row tiles).
+_PATHS = [(BF16, 1), (BF16, 2), (FP32, 0)]
+
+
+@pytest.mark.parametrize("name", ["spec", "mixed", "decode"])
+@pytest.mark.parametrize("dtype,kind", _PATHS)
+def test_paging_invariance_and_determinism(name, dtype, kind):
     """Permuted physical blocks vs a contiguous per-sequence layout: bit-identical GPU output; two runs
-    of the same call are bit-identical too."""
-    w = make_config("spec", "small")
-    log("paging invariance (spec small)")
+    of the same call are bit-identical too; and the result matches the oracle.  Under every kernel."""
+    pkv.set_tuning(0, 0, kind)
+    w = make_config(name, "small", dtype=dtype)
+    log(f"paging invariance ({name} small, {dtype}, tile kind {kind})")
     dw = DeviceWorkload(w)
     out1 = dw.run_step(0).clone()
     st = dw.steps[0]
@@ -170,12 +177,18 @@ def test_paging_invariance_and_determinism():
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
     assert torch.equal(out1, out3)
+    _, _, outs = _oracle_steps(w)
+    check_close(out_f64(out1), outs[0], dtype, f"paging {name} {dtype} kind={kind}")
 
 
-def test_garbage_invariance():
-    """NaN in every pool row no sequence uses, and -1 past each table's blocks: same output, finite."""
-    w = make_config("decode", "small")
-    log("garbage invariance")
+@pytest.mark.parametrize("name", ["decode", "spec", "mixed"])
+@pytest.mark.parametrize("dtype,kind", _PATHS)
+def test_garbage_invariance(name, dtype, kind):
+    """NaN in every pool row no sequence uses (whole unowned blocks and the rows past each context in its
+    last block), and -1 past each table's blocks: same output, finite.  Under every kernel."""
+    pkv.set_tuning(0, 0, kind)
+    w = make_config(name, "small", dtype=dtype)
+    log(f"garbage invariance ({name} small, {dtype}, tile kind {kind})")
     dw = DeviceWorkload(w)
     out1 = dw.run_step(0).clone()
     L = w.steps[0].context_lens
@@ -183,6 +196,7 @@ def test_garbage_invariance():
     for s in range(w.num_seqs):
         for p in range(int(L[s])):
             used[w.block_tables[s][p // w.block_size], p % w.block_size] = True
+    assert np.all(w.block_tables[w.block_tables < 0] == -1)
     mask = torch.from_numpy(~used).to(dw.k_pool.device)
     kp = dw.k_pool.clone()
     vp = dw.v_pool.clone()
@@ -226,8 +240,10 @@ def test_shared_prefix_equals_private_copy():
                                                    ("spec", 2, 1), ("tiny", 3, 2)])
 def test_layer_inside_block_pool(workload, layers, layer):
     """The pool layout [num_blocks, layers, block_size, H_kv, D] (layer inside the block, "Paged
-    Attention 基础 – 原理与实现进度" §4) addressed through block_stride gives bit for bit the result and
-    the pool contents of the per-layer pool, and leaves the other layers untouched."""
+    Attention 基础 – 原理与实现进度" §4) addressed through block_stride: its attention output matches the
+    oracle (which walks the per-layer pool the layer slice holds), its pool slice holds exactly the oracle's
+    pool after each write, the result is bit for bit the per-layer pool's, and the other layers stay
+    untouched."""
     w = make_config(workload, "small")
     log(f"layer-inside-block pool {workload} layers={layers} layer={layer}")
     dw = DeviceWorkload(w)
@@ -236,6 +252,7 @@ def test_layer_inside_block_pool(workload, layers, layer):
     big_v = torch.zeros_like(big_k)
     big_k[:, layer] = dw.k_pool
     big_v[:, layer] = dw.v_pool
+    okp, ovp = w.k_pool, w.v_pool
     for i, st in enumerate(dw.steps):
         out_ref = dw.run_step(i).clone()
         pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], big_k[:, layer], big_v[:, layer])
@@ -243,6 +260,11 @@ def test_layer_inside_block_pool(workload, layers, layer):
                                           st["context_lens"], st["query_start_loc"], scale=w.scale,
                                           max_q_len=st["max_q_len"])
         torch.cuda.synchronize()
+        okp, ovp, ref = oracle.run_step(okp, ovp, w.block_tables, w.steps[i], w.scale, w.dtype)
+        check_close(out_f64(out), ref, w.dtype, f"layer-inside-block {workload} step {i}")
+        bits = (lambda a: a.view(np.uint32)) if w.dtype == FP32 else (lambda a: a)
+        assert np.array_equal(pool_bits(big_k[:, layer].contiguous()), bits(okp))
+        assert np.array_equal(pool_bits(big_v[:, layer].contiguous()), bits(ovp))
         assert torch.equal(out, out_ref)
         assert torch.equal(big_k[:, layer], dw.k_pool) and torch.equal(big_v[:, layer], dw.v_pool)
     for other in range(layers):
@@ -319,3 +341,52 @@ def test_empty_and_degenerate():
                                 torch.empty(0, dtype=torch.int32, device=d),
                                 torch.zeros(1, dtype=torch.int32, device=d))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("partition", [0, 64])
+@pytest.mark.parametrize("kind", [1, 2])
+def test_many_sequences(kind, partition):
+    """More sequences than the planner keeps in LDS (2048): 3000 short decode and speculative sequences,
+    so the planner reads the later ones' metadata from global memory, with automatic and forced partitions
+    under both tile kinds."""
+    rng = np.random.default_rng(41)
+    N = 3000
+    q_lens = rng.choice([1, 1, 1, 2, 4, 7], N)
+    ctx = q_lens + rng.integers(0, 200, N)
+    w = build_workload(rng, name="many", dtype=BF16, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                       block_size=16, q_lens=q_lens, context_lens=ctx)
+    log(f"{N} sequences, tile kind {kind}, partition {partition}")
+    pkv.set_tuning(partition, 0, kind)
+    dw = DeviceWorkload(w)
+    out = dw.run_step(0)
+    torch.cuda.synchronize()
+    _, _, outs = _oracle_steps(w)
+    check_close(out_f64(out), outs[0], BF16, f"{N} sequences kind={kind} P={partition}")
+
+
+@pytest.mark.parametrize("dtype,kind", _PATHS)
+def test_rejected_sequences_give_nan_rows(dtype, kind):
+    """Sequences whose metadata the library rejects (more new tokens than cached ones, a negative context,
+    a context longer than the table) get NaN output rows; the other sequences' rows are still right."""
+    pkv.set_tuning(0, 0, kind)
+    w = build_workload(np.random.default_rng(43), name="bad", dtype=dtype, num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, q_lens=[3, 2, 1, 4, 1], context_lens=[40, 30, 60, 20, 9])
+    log(f"rejected sequences ({dtype}, tile kind {kind})")
+    dw = DeviceWorkload(w)
+    st = dw.steps[0]
+    pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], dw.k_pool, dw.v_pool)
+    ctx = w.steps[0].context_lens.copy()
+    ctx[1] = 1                                              # q_len 2 > context 1
+    ctx[3] = -5                                             # negative context
+    ctx[4] = w.block_tables.shape[1] * w.block_size + 1     # past the table
+    out = torch.full_like(st["q"], 7.0)
+    pkv.paged_attention_forward(st["q"], dw.k_pool, dw.v_pool, dw.block_tables, to_torch(ctx, None),
+                                st["query_start_loc"], scale=w.scale, out=out, max_q_len=st["max_q_len"])
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    qsl = w.steps[0].query_start_loc
+    for s in (1, 3, 4):
+        assert np.all(np.isnan(got[qsl[s]:qsl[s + 1]])), s
+    _, _, ref = oracle.run_step(w.k_pool, w.v_pool, w.block_tables, w.steps[0], w.scale, w.dtype, seqs=[0, 2])
+    good = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in (0, 2)])
+    check_close(got[good], ref[good], dtype, "valid sequences beside rejected ones")
