@@ -41,9 +41,12 @@
  *    of num_kv_heads (query head h reads kv head h / (num_q_heads / num_kv_heads)); num_blocks *
  *    block_size < 2^31; every data pointer and block_stride * element size 16-byte aligned.
  *  - Contents of device metadata are trusted: a block id outside [0, num_blocks) among a sequence's first
- *    ceil(context_len / block_size) table entries, a slot outside the pool, q_len > context_len, a
- *    decreasing query_start_loc, or a slot repeated within one write are outside the supported inputs
- *    (behaviour undefined; the Python binding's validate=True mode checks them on the host first).
+ *    ceil(context_len / block_size) table entries, a slot outside the pool, a decreasing
+ *    query_start_loc, or a slot repeated within one write are outside the supported inputs (behaviour
+ *    undefined; the Python binding's validate=True mode checks them on the host first).  A sequence the
+ *    attention call rejects on the device -- q_len > context_len, a negative context_len, or context_len >
+ *    max_blocks_per_seq * block_size -- reads nothing and gets NaN in every output row, when its own
+ *    query_start_loc range lies inside [0, total_q]; the other sequences are computed as usual.
  */
 #ifndef PAGED_KV_H
 #define PAGED_KV_H

@@ -31,7 +31,15 @@ __global__ void __launch_bounds__(64) attn_fp32_kernel(const AttnParams p) {
   const int q0 = qsl[s];
   const int n = qsl[s + 1] - q0;
   const int L = p.context_lens[s];
-  if (n <= 0 || n > L || L > p.max_blocks_per_seq << p.block_size_log2) return;
+  if (n <= 0) return;
+  if (n > L || L > p.max_blocks_per_seq << p.block_size_log2) {
+    // Rejected metadata (more new tokens than cached ones, or a context past the table): the row is NaN so
+    // that the error shows in the result.
+    float* orow = static_cast<float*>(p.out) + (static_cast<int64_t>(tok) * p.num_q_heads + h) * D;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) orow[lane + 64 * c] = __builtin_nanf("");
+    return;
+  }
   const int i = tok - q0;
   const int lim = L - n + i;  // keys 0 .. lim
   const int g = h / p.group;

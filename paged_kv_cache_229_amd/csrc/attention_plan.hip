@@ -23,6 +23,7 @@
 //
 // The method's softmax is "Paged Attention 基础 – 原理与实现进度", §2 step 5; splitting the key range and
 // merging the partial softmax sums gives the same result up to float32 rounding order.
+#include "fastdiv.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -52,26 +53,6 @@ struct TileGeom {
     if (end >= rows) return L;
     if (tokens_per_tile > 0) return L - n + (t + 1) * tokens_per_tile;
     return L - n + (end - 1) / G + 1;
-  }
-};
-
-// Division by a divisor fixed for many calls (2 <= d < 2^31): q = mulhi(n, m) with m = floor((2^32 - 1)
-// / d) + 1 is floor(n / d) or one more, since n m / 2^32 lies in [n / d, n / d + 1); one compare fixes it.
-struct FastDiv {
-  unsigned d, m;
-  __device__ explicit FastDiv(int divisor)
-      : d(static_cast<unsigned>(divisor)), m(0xffffffffu / static_cast<unsigned>(divisor) + 1u) {}
-  __device__ int floor_div(int n) const {
-    unsigned q = __umulhi(static_cast<unsigned>(n), m);
-    q -= q * d > static_cast<unsigned>(n) ? 1u : 0u;
-    return static_cast<int>(q);
-  }
-  // ceil(n / d) for 0 <= n < 2^31.
-  __device__ int ceil_div(int n) const {
-    const unsigned a = static_cast<unsigned>(n) + d - 1u;
-    unsigned q = __umulhi(a, m);
-    q -= q * d > a ? 1u : 0u;
-    return static_cast<int>(q);
   }
 };
 
@@ -443,6 +424,36 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     p.buf.hdr[kHdrPrefTable] = pb;
     p.buf.hdr[kHdrPrefPartition] = Pv;
     p.buf.hdr[kHdrPrefParts] = npv;
+  }
+
+  // Rejected sequences (q_len > context, negative context, context past the table) get NaN output rows,
+  // so that bad metadata shows in the result without a host check.  A sequence whose query range itself
+  // is inconsistent owns no rows and is left alone.  Each wave takes its own sequences; a wave-wide loop
+  // fills the rows of each rejected one.  Rare: skipped unless the first pass found a rejected sequence.
+  if (total_bad > 0 && p.out != nullptr) {
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};  // eight bf16 NaNs
+    const int lane = tid & 63;
+    for (int base = tid - lane; base < N; base += kPlanThreads) {
+      const int s = base + lane;
+      int lo = 0, hi = 0;
+      bool poison = false;
+      if (s < N) {
+        lo = qsl[s];
+        hi = qsl[s + 1];
+        poison = lo >= 0 && hi > lo && hi <= p.total_q && !seq_ok(lo, hi, ctx[s], p.total_q, p.max_context);
+      }
+      unsigned long long m = __builtin_amdgcn_ballot_w64(poison);
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        const int blo = __builtin_amdgcn_readlane(lo, b);
+        const int bhi = __builtin_amdgcn_readlane(hi, b);
+        u32x4v* const o = static_cast<u32x4v*>(p.out) + static_cast<int64_t>(blo) * p.out_row_chunks;
+        const int64_t chunks = static_cast<int64_t>(bhi - blo) * p.out_row_chunks;
+        for (int64_t c = lane; c < chunks; c += 64) o[c] = nan8;
+      }
+    }
   }
 }
 

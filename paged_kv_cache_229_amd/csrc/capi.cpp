@@ -166,7 +166,8 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
     return fail(PKV_ERR_INVALID_ARG, "k, v, k_cache, v_cache must be 16-byte aligned");
   const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * elem_bytes(dtype);
   const int64_t cpr = row_bytes / 16;
-  if (num_tokens * 2 * cpr > INT32_MAX)
+  // The kernel strides over the 16-byte chunks with a 32-bit index: the last stride must not overflow.
+  if (num_tokens > (int64_t{INT32_MAX} - pkv::kWriteGridLanes) / (2 * cpr))
     return fail(PKV_ERR_UNSUPPORTED, "num_tokens * row size too large for one call; split the write");
   pkv::KvWriteParams p{};
   p.k = k;
@@ -328,6 +329,8 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   pp.prow_cap = pkv::kPartialRowCap;
   if (prefix) pp.prefix = *prefix;
   pp.buf = b;
+  pp.out = out;
+  pp.out_row_chunks = num_q_heads * head_dim * 2 / 16;
 
   hipError_t e = pkv::launch_plan(pp, st);
   if (e != hipSuccess) return hip_fail("plan launch", e);

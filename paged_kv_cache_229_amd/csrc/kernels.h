@@ -10,6 +10,10 @@ namespace pkv {
 // of it.
 constexpr int kStageKeys = 64;
 constexpr int kThreads = 256;
+// paged_kv_write's grid: at most this many workgroups of kThreads lanes, striding over 16-byte chunks with a
+// 32-bit index, so a call may move at most INT32_MAX - kWriteGridLanes chunks.
+constexpr int kWriteMaxBlocks = 8192;
+constexpr int kWriteGridLanes = kWriteMaxBlocks * kThreads;
 // Row-tile kinds of the bf16 attention.  Kind 1: 128-row tiles, 8 waves of 16 rows (two waves per SIMD),
 // for rows-poor batches (decode, speculative decode).  Kind 2: 256-row tiles, 8 waves of 32 rows (two
 // waves per SIMD, 32 x 32 MFMA tiles), for long query chunks.
@@ -100,6 +104,11 @@ struct PlanParams {
   int prow_cap;
   PrefixParams prefix;
   PlanBuffers buf;
+  // Output rows of sequences the plan rejects (q_len > context, negative context, context past the table)
+  // are filled with NaN when their query range is consistent: out is [total_q][out_row_chunks] 16-byte
+  // chunks of bf16.
+  void* out;
+  int out_row_chunks;
 };
 
 struct AttnParams {

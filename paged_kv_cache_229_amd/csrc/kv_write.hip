@@ -21,6 +21,7 @@ __global__ void __launch_bounds__(kThreads) kv_write_kernel(const KvWriteParams 
   const int total = p.num_tokens * per_token;
   const int64_t row_bytes = static_cast<int64_t>(cpr) * 16;
   const int bs_mask = (1 << p.block_size_log2) - 1;
+  // 32-bit index: the host keeps total + one grid stride below 2^31.
   for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < total; idx += gridDim.x * kThreads) {
     const int t = idx / per_token;
     const int rem = idx - t * per_token;
@@ -43,7 +44,7 @@ hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream) {
   if (p.num_tokens == 0) return hipSuccess;
   const int64_t total = static_cast<int64_t>(p.num_tokens) * 2 * p.chunks_per_row;
   int64_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > kWriteMaxBlocks) blocks = kWriteMaxBlocks;
   hipLaunchKernelGGL(kv_write_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                      p);
   return hipGetLastError();

@@ -192,3 +192,14 @@ def test_validate_metadata_host_checks():
                 dict(block_tables=torch.tensor([[0, 9], [2, -1]], dtype=torch.int32))):
         with pytest.raises(ValueError):
             pkv.validate_metadata(**{**ok, **bad})
+
+
+def test_write_limit_keeps_the_kernel_index_in_32_bits():
+    """paged_kv_write strides over 16-byte chunks with a 32-bit index: the host refuses a call whose chunk
+    count plus one grid stride (8192 workgroups x 256 lanes) would pass 2^31 - 1, before any HIP call."""
+    cpr = 8 * 128 * 2 // 16                         # 16-byte chunks per K row at H_kv 8, D 128, bf16
+    limit = (2 ** 31 - 1 - 8192 * 256) // (2 * cpr)  # largest accepted token count
+    assert _write(T=limit + 1, hkv=8, d=128) == N.PKV_ERR_UNSUPPORTED
+    assert _write(T=(2 ** 31 - 1) // (2 * cpr), hkv=8, d=128) == N.PKV_ERR_UNSUPPORTED
+    assert _write(T=2 ** 40, hkv=8, d=128) == N.PKV_ERR_UNSUPPORTED
+    assert _write(T=limit, hkv=8, d=128, kc=0) == N.PKV_ERR_INVALID_ARG  # accepted size, fails on the null pool
