@@ -24,7 +24,8 @@
  * Conventions shared by every entry point:
  *
  *  - Pointers marked (device) are HIP device addresses; (host) are host addresses.  The caller owns every
- *    buffer.  The library allocates no memory and keeps no pointer after a call returns.
+ *    buffer.  The library allocates no memory and keeps no pointer after a call returns (its one buffer
+ *    of its own is paged_attention_forward_noalloc's fixed scratch, below).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work on it and return at once;
  *    no call synchronises the device.
  *  - The return value is a pkv_status.  A negative status means nothing was enqueued; the reason is in
@@ -137,6 +138,40 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                             int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
                             int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Size in bytes of the library's own device scratch used by paged_attention_forward_noalloc (32 MiB per
+ * GPU).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES 33554432
+
+/*
+ * paged_attention_forward_noalloc — paged_attention_forward (same arguments and result, up to float32
+ * summation order) without a workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It calls no allocating
+ * routine.  Its scratch (the per-call work plan and split-context partial rows) is a fixed buffer of
+ * PKV_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, that each GPU holds from the library's first
+ * use on it until the process ends.
+ *
+ *  - Size limit: the call's work records (a few hundred bytes per sequence and per 128 query rows of a
+ *    kv head, see paged_attention_workspace_size) must fit the scratch with room to spare, else
+ *    PKV_ERR_UNSUPPORTED and nothing is enqueued; what remains holds up to 131072 partial rows (about
+ *    63000 at head_dim 128), fewer than with a full workspace, so long contexts may be split into fewer,
+ *    longer partitions.
+ *  - All calls on one GPU share that GPU's scratch, whatever the stream: calls that overlap on one GPU
+ *    race (and give undefined output); order them on one stream or synchronise between them.  Each call
+ *    initialises what it reads, so the previous call's leftovers never matter.
+ *  - The first call on a device looks up the scratch's device address (hipGetSymbolAddress) with that
+ *    device current; a failure there returns PKV_ERR_HIP.
+ * PKV_FP32 needs no scratch and runs as paged_attention_forward.
+ */
+int paged_attention_forward_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, const int32_t* query_start_loc,
+                                    int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
+                                    int32_t max_q_len_hint, void* stream);
 
 /*
  * Bytes of device workspace paged_attention_forward_prefix needs (0 for PKV_FP32).  Returns 0 and sets

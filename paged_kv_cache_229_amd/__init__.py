@@ -7,6 +7,8 @@ the library's kernels.  PyTorch supplies device memory and streams.
     paged_kv_write(k, v, slot_mapping, k_cache, v_cache)
     out = paged_attention_forward(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
                                   scale=None)
+    paged_attention_forward_noalloc(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                                    out)                       # no workspace: the library's fixed scratch
     mgr = CacheManager(num_blocks, block_size)        # host block allocator, tables, slot mapping
     slots, cow = mgr.append(seq_id, num_tokens)       # cow: (src, dst) block to copy_blocks() first
 
@@ -41,6 +43,7 @@ __all__ = [
     "paged_kv_write",
     "paged_attention_forward",
     "paged_attention_forward_prefix",
+    "paged_attention_forward_noalloc",
     "workspace_size",
     "prefix_workspace_size",
     "set_tuning",
@@ -189,6 +192,23 @@ def paged_attention_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q,
         hq, hkv, d, bs, nb, stride, scale, _dtype_code(q), hint, workspace.data_ptr(),
         workspace.numel(), _stream(dev)))
+    return out
+
+
+def paged_attention_forward_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                    block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                    query_start_loc: torch.Tensor, out: torch.Tensor, scale: float | None = None,
+                                    max_q_len: int | None = None, validate: bool = False) -> torch.Tensor:
+    """``paged_attention_forward`` into the caller's ``out`` with no workspace and no device allocation in
+    the library (its fixed per-GPU scratch instead; calls on one GPU must not overlap); see
+    ``paged_attention_forward_noalloc`` in include/paged_kv.h."""
+    dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, scale = _attention_args(
+        q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, validate)
+    hint = -1 if max_q_len is None else int(max_q_len)
+    check(lib().paged_attention_forward_noalloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q,
+        hq, hkv, d, bs, nb, stride, scale, _dtype_code(q), hint, _stream(dev)))
     return out
 
 

@@ -22,6 +22,7 @@ PKV_ERR_HIP = -4
 PKV_ERR_NO_BLOCKS = -5
 PKV_FP32 = 0
 PKV_BF16 = 1
+PKV_NOALLOC_SCRATCH_BYTES = 33554432
 
 STATUS_NAMES = {
     PKV_OK: "PKV_OK",
@@ -44,6 +45,8 @@ SIGNATURES = {
     "paged_attention_forward": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
                                            _i32, _i32, _i32, _i64, _i64, _f32, _i32, _i32, _vp, _sz,
                                            _vp]),
+    "paged_attention_forward_noalloc": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
+                                                   _i32, _i32, _i32, _i64, _i64, _f32, _i32, _i32, _vp]),
     "paged_attention_prefix_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "paged_attention_forward_prefix": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
                                                   _i32, _i32, _i32, _i32, _i64, _i64, _f32, _i32, _i32,

@@ -7,6 +7,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -14,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 thread_local std::string g_error;
 thread_local int g_partition_keys = 0;
@@ -84,7 +85,7 @@ int check_pool(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_
 struct WsLayout {
   size_t hdr, seq_tiles, tile_rec, units, part_ml, part_acc, tok_info, total;
   int rows_per_tile;
-  int64_t tile_cap, unit_cap;
+  int64_t tile_cap, unit_cap, prow_cap;
 };
 
 // Tile kind 1 (128-row tiles) when the hint says every sequence's rows (q_len x group) fit one such
@@ -96,8 +97,9 @@ int choose_tile_kind(int group, int64_t total_q, int32_t max_q_len_hint) {
 }
 
 WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
-                          int32_t head_dim, int tile_kind) {
+                          int32_t head_dim, int tile_kind, int64_t partial_rows = pkv::kPartialRowCap) {
   WsLayout w{};
+  w.prow_cap = partial_rows;
   const int group = num_q_heads / num_kv_heads;
   w.rows_per_tile = pkv::tile_rows_of(tile_kind);
   // Each sequence adds at most one partly filled tile.
@@ -114,7 +116,7 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   off = round256(off + static_cast<size_t>(w.tile_cap) * 4 * sizeof(int));
   w.units = off;
   off = round256(off + static_cast<size_t>(w.unit_cap) * 8 * sizeof(int));
-  const size_t part_rows = pkv::kPartialRowCap;
+  const size_t part_rows = static_cast<size_t>(partial_rows);
   w.part_ml = off;
   off = round256(off + part_rows * 2 * sizeof(float));
   w.part_acc = off;
@@ -140,6 +142,35 @@ int num_cus() {
 
 int hip_fail(const char* what, hipError_t e) {
   return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Device scratch of paged_attention_forward_noalloc, in place of a caller's workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code `scratch` only names the
+// variable: its device address, per device, comes from hipGetSymbolAddress (scratch_address below) and
+// is what the kernels are given.
+constexpr size_t kScratchBytes = size_t{PKV_NOALLOC_SCRATCH_BYTES};
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device (with that device current).
+int scratch_address(void** addr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", g);
+    if (p == nullptr) return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return PKV_OK;
 }
 
 }  // namespace
@@ -240,7 +271,8 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
                    const int32_t* query_start_loc, int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                    int64_t block_stride, float scale, int32_t dtype, int32_t max_q_len_hint,
-                   const pkv::PrefixParams* prefix, void* workspace, size_t workspace_bytes, void* stream) {
+                   const pkv::PrefixParams* prefix, void* workspace, size_t workspace_bytes, void* stream,
+                   bool noalloc = false) {
   if (num_seqs < 0 || total_q < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs and total_q must be >= 0");
   int64_t stride = 0;
   const int rc = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
@@ -292,7 +324,23 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   }
 
   const int tile_kind = prefix ? 2 : choose_tile_kind(group, total_q, max_q_len_hint);
-  const WsLayout w = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind);
+  WsLayout w = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind);
+  if (noalloc) {
+    // The library's scratch: the per-call records must fit; the rest holds as many partial rows as it
+    // can (fewer partial rows only make the plan split long contexts into fewer partitions).
+    const WsLayout fixed = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind, 0);
+    if (fixed.total + 512 > kScratchBytes)
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attention_forward_noalloc: this call's work records need " +
+                                           std::to_string(fixed.total) + " bytes, more than the " +
+                                           std::to_string(kScratchBytes) + "-byte scratch; use "
+                                           "paged_attention_forward with a workspace");
+    const int64_t rows = static_cast<int64_t>((kScratchBytes - fixed.total - 512) / (8 + 4 * head_dim));
+    w = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind,
+                         rows < pkv::kPartialRowCap ? rows : pkv::kPartialRowCap);
+    const int st = scratch_address(&workspace);
+    if (st != PKV_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < w.total)
     return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(w.total) + " bytes, got " +
                                        std::to_string(workspace_bytes));
@@ -326,7 +374,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   pp.forced_partition = g_partition_keys;
   pp.unit_cap = static_cast<int>(w.unit_cap);
   pp.tile_cap = static_cast<int>(w.tile_cap);
-  pp.prow_cap = pkv::kPartialRowCap;
+  pp.prow_cap = static_cast<int>(w.prow_cap);
   if (prefix) pp.prefix = *prefix;
   pp.buf = b;
   pp.out = out;
@@ -362,6 +410,19 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                         query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
                         num_blocks, block_stride, scale, dtype, max_q_len_hint, nullptr, workspace,
                         workspace_bytes, stream);
+}
+
+int paged_attention_forward_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, const int32_t* query_start_loc,
+                                    int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
+                                    int32_t max_q_len_hint, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, block_stride, scale, dtype, max_q_len_hint, nullptr, nullptr, 0, stream,
+                        /*noalloc=*/true);
 }
 
 size_t paged_attention_prefix_workspace_size(int32_t num_seqs, int64_t total_q, int32_t num_q_heads,

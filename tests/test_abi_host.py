@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
         assert name in N.SIGNATURES, f"{name} declared in the header but not bound"
         assert hasattr(lib, name), f"{name} not exported"
     assert set(N.SIGNATURES) == set(names)
-    assert lib.paged_kv_abi_version() == 3
+    assert lib.paged_kv_abi_version() == 4
 
 
 def test_single_hip_runtime_loaded():
@@ -203,3 +203,18 @@ def test_write_limit_keeps_the_kernel_index_in_32_bits():
     assert _write(T=(2 ** 31 - 1) // (2 * cpr), hkv=8, d=128) == N.PKV_ERR_UNSUPPORTED
     assert _write(T=2 ** 40, hkv=8, d=128) == N.PKV_ERR_UNSUPPORTED
     assert _write(T=limit, hkv=8, d=128, kc=0) == N.PKV_ERR_INVALID_ARG  # accepted size, fails on the null pool
+
+
+def test_noalloc_rejects_calls_whose_records_exceed_its_scratch():
+    """paged_attention_forward_noalloc refuses, on the host and before any HIP call, a call whose per-call
+    work records would not fit the library's fixed scratch (PKV_NOALLOC_SCRATCH_BYTES)."""
+    lib = N.lib()
+    n = 400_000  # ~100 bytes of records per single-token sequence: more than 32 MiB
+    rc = lib.paged_attention_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, n, n, 8, 2, 128, 16,
+                                             1024, 0, 0.1, N.PKV_BF16, 1, None)
+    assert rc == N.PKV_ERR_UNSUPPORTED
+    assert b"scratch" in lib.paged_kv_last_error()
+    # argument errors come first, as in paged_attention_forward
+    rc = lib.paged_attention_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 4, 4, 8, 3, 128, 16,
+                                             1024, 0, 0.1, N.PKV_BF16, 1, None)
+    assert rc == N.PKV_ERR_INVALID_ARG
