@@ -68,7 +68,10 @@ def recorded_traffic(workload: str):
         rec = json.load(f)
     h = hashlib.sha256()
     for src in rec.get("sources", []):
-        with open(os.path.join(ROOT, src), "rb") as f:
+        path = os.path.join(ROOT, src)
+        if not os.path.exists(path):  # a source the counters covered is gone: the record is stale
+            return None
+        with open(path, "rb") as f:
             h.update(f.read())
     if h.hexdigest() != rec.get("kernel_source_sha256"):
         return None
@@ -227,14 +230,9 @@ def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, pr
 
 
 def kernel_name_for(w, tile_kind: int = 0, prefix_pass: bool = False) -> str:
-    """The attention kernel the library runs for this workload: the 16-row one when every sequence's rows
-    (q_len x group) fit a 128-row tile, the 32x32 one otherwise (its automatic rule, given the q-length
-    hint the bench passes); the shared-prefix pass always uses 256-row tiles."""
-    import numpy as np
-    if prefix_pass:
-        return "attn_wide_kernel"
-    max_rows = int(np.diff(w.steps[0].query_start_loc).max()) * (w.num_q_heads // w.num_kv_heads)
-    return "attn_bf16_kernel" if (tile_kind or (1 if max_rows <= 128 else 2)) == 1 else "attn_wide_kernel"
+    """The attention kernel that runs the workload's work items (one kernel; each item runs the 16-row or the
+    32-row body its sequence's tile kind selects)."""
+    return "attn_kernel"
 
 
 def hbm_view(dev, name: str, steps: int, warmup: int, copies: int) -> dict:

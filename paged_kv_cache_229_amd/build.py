@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["capi.cpp", "cache_manager.cpp", "kv_write.hip", "copy_blocks.hip", "attention_plan.hip",
-           "attention_bf16.hip", "attention_wide.hip", "attention_fp32.hip"]
+           "attention.hip", "attention_fp32.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -43,7 +43,7 @@ COMMON_FLAGS = [
 # output either way.  Their work-queue pops are single-lane atomics whose results are consumed after an
 # explicit wait; the atomic optimiser would turn each into a wave reduction that waits at once.
 _ATTN_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
-EXTRA_FLAGS = {"attention_bf16.hip": _ATTN_FLAGS, "attention_wide.hip": _ATTN_FLAGS}
+EXTRA_FLAGS = {"attention.hip": _ATTN_FLAGS}
 
 
 def hipcc() -> str:

@@ -8,8 +8,10 @@
 // (ADR 004 "Paged Attention Serving Integration", Consequences: prefill and decode share one call) and
 // grouped kv heads (the same comment: MQA/GQA) are handled by one kernel.
 //
-// This kernel serves row tiles of 128 rows (decode, speculative decode); long query chunks go to
-// attention_wide.hip, which runs the same pipeline on 32 x 32 MFMA tiles.
+// This item body serves row tiles of 128 rows (decode, speculative decode, and any sequence whose q_len x
+// group rows fit one such tile); taller tiles (long query chunks) go to the body in attention_wide.h, which
+// runs the same pipeline on 32 x 32 MFMA tiles.  attention.hip runs both in one persistent kernel and picks
+// the body per work item from the unit's tile kind.
 //
 // How (gfx950 design, not a translation of any kernel the pages name):
 //  * Work item = (unit, kv head) from the device plan; a persistent grid pops items from a queue.  The
@@ -34,6 +36,8 @@
 //    few (decode); in the latter case the waves' softmax states are merged through LDS at the end.
 //  * A tile whose context was split into partitions writes (acc, m, l) per row; split_reduce_kernel
 //    merges them.  Unsplit tiles write the normalised bf16 output directly.
+#pragma once
+
 #include <type_traits>
 
 #include "device_util.h"
@@ -65,12 +69,13 @@ struct Geo {
   static_assert(NL >= 1 && KPW % KPL == 0, "stage split");
 };
 
-template <int D, int NTW>
-__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bf16_kernel(const AttnParams p) {
+// One work item (unit, kv head g) on 16-row waves.  Every thread of the workgroup calls it; `smem` is the
+// workgroup's ring (at least Geo<D, NTW>::SMEM bytes of LDS); thread 0 claims the next item into
+// `next_item` once the item's last stage is consumed.
+template <int D, int NTW = 1>
+__device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords& pw, unsigned char* smem,
+                                            int unit, int g, int& next_item) {
   using T = Geo<D, NTW>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::SMEM];
-  __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -80,9 +85,8 @@ attn_bf16_kernel(const AttnParams p) {
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
   const int Hq = p.num_q_heads;
-  const int total_items = p.buf.hdr[kHdrUnits] * Hkv;
-  const int P = p.buf.hdr[kHdrPartition];
-  const int Pw = p.buf.hdr[kHdrPartitionWide];
+  const int P = pw.P;
+  const int Pw = pw.Pw;
   const int bs_log2 = p.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int last_block = static_cast<int>(p.num_blocks - 1);
@@ -115,21 +119,9 @@ attn_bf16_kernel(const AttnParams p) {
   for (int t = 0; t < 8; ++t) ones[t] = static_cast<__bf16>(1.f);
   const float inv_sl2 = 1.f / sl2;
 
-  // The next item is claimed while the current one finishes (after its last stage), so the atomic's
-  // latency hides behind the epilogue.
-  int next_item = 0;
-  if (tid == 0) next_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
-  for (;;) {
-    if (tid == 0) s_item = next_item;
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
-    __syncthreads();
-    if (item >= total_items) break;
-
+  {
     // The plan's arrays are read-only here: scalar loads (constant address space) keep these reads off
     // the vector-memory counter.
-    const int unit = item / Hkv;
-    const int g = item - unit * Hkv;
     const CONST_AS int* const urec = (const CONST_AS int*)p.buf.units + 8 * unit;
     const int s = urec[0], tile = urec[1], kb = urec[2], pbase = urec[3];
     const int q0 = urec[4];  // the sequence's first query token, query tokens and context, from the plan
@@ -425,24 +417,6 @@ attn_bf16_kernel(const AttnParams p) {
   }
 }
 
+
 }  // namespace
-
-int attention_bf16_wgs_per_cu(int head_dim, int tile_kind) {
-  if (tile_kind == 2) return attention_wide_wgs_per_cu(head_dim);
-  // 160 KiB of LDS per CU; a workgroup holds the 4-stage K/V ring (reused for the merge) plus a word.
-  const int smem = head_dim == 128 ? Geo<128, 1>::SMEM : Geo<64, 1>::SMEM;
-  const int lds = smem + 64;
-  int wgs = (160 * 1024) / lds;
-  return wgs < 1 ? 1 : (wgs > 2 ? 2 : wgs);
-}
-
-hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
-                                 hipStream_t stream) {
-  if (tile_kind == 2) return launch_attention_wide(p, head_dim, grid, stream);
-  const dim3 g(static_cast<unsigned>(grid)), b(kAttnThreads);
-  if (head_dim == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), g, b, 0, stream, p);
-  else hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), g, b, 0, stream, p);
-  return hipGetLastError();
-}
-
 }  // namespace pkv

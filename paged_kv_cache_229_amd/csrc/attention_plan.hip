@@ -6,8 +6,10 @@
 //   unit = (sequence s, row tile t, context partition p), processed once per kv head.
 //
 // The rows of (s, kv head g) are the pairs (query token i, query head of g's group), row = i * G + h',
-// so a tile holds several tokens' worth of grouped heads and the keys it loads serve all of them.  Row
-// tile t covers rows [t*RT, min(rows, (t+1)*RT)); its last token sees keys [0, kmax).  A tile whose kmax
+// so a tile holds several tokens' worth of grouped heads and the keys it loads serve all of them.  A
+// sequence's tiles are 128 rows high when its rows fit one such tile, else 256 (tile_kind_for; the unit
+// record carries the kind, which picks the item body of the attention kernel).  Row tile t covers rows
+// [t*RT, min(rows, (t+1)*RT)); its last token sees keys [0, kmax).  A tile whose kmax
 // exceeds its partition length is split into ceil(kmax / length) partitions.  Tiles of at most
 // kSmallTileRows rows (decode-like work) use P, picked so the whole call has about `target_items`
 // (unit, kv head) items, enough to fill 256 compute units several times over, but no shorter than
@@ -48,6 +50,8 @@ __device__ inline bool seq_ok(int q_lo, int q_hi, int context_len, int64_t total
 // division is needed; the last tile's last row is the last token, which sees all L keys.
 struct TileGeom {
   int G, RT, tokens_per_tile;  // tokens_per_tile = RT / G when G divides RT, else 0
+  int kind, rt_log2;
+  __device__ int tiles(int rows) const { return (rows + RT - 1) >> rt_log2; }
   __device__ int kmax(int L, int n, int rows, int t) const {
     const int end = (t + 1) * RT;
     if (end >= rows) return L;
@@ -142,12 +146,15 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   const int tid = threadIdx.x;
   __shared__ int red[kPlanWaves];
   const int N = p.num_seqs;
-  const int RT = p.rows_per_tile;
   const int G = p.group;
   const int Hkv = p.num_kv_heads;
   const int* const qsl = p.query_start_loc;
   const int* const ctx = p.context_lens;
-  const TileGeom geo{G, RT, RT % G == 0 ? RT / G : 0};
+  // Tile geometry of each kind; a sequence takes the one tile_kind_for gives its rows.
+  const TileGeom geo1{G, tile_rows_of(1), tile_rows_of(1) % G == 0 ? tile_rows_of(1) / G : 0, 1, 7};
+  const TileGeom geo2{G, tile_rows_of(2), tile_rows_of(2) % G == 0 ? tile_rows_of(2) / G : 0, 2, 8};
+  static_assert(tile_rows_of(1) == 1 << 7 && tile_rows_of(2) == 1 << 8, "tile heights");
+  auto geom = [&](int rows) -> TileGeom { return tile_kind_for(rows, p.tile_kind) == 1 ? geo1 : geo2; };
   // Per-thread partial counts only ever meet caps below 2^17; saturating them at 2^22 keeps every
   // workgroup sum (256 threads) in 32 bits.
   constexpr int kSat = 1 << 22;
@@ -191,7 +198,8 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       ++bad;
     } else if (n > 0) {
       const int rows = n * G;
-      nt = (rows + RT - 1) / RT;
+      const TileGeom geo = geom(rows);
+      nt = geo.tiles(rows);
       for (int t = 0; t < nt; ++t) work = min(work + (geo.kmax(L, n, rows, t) + kStageKeys - 1) / kStageKeys, kSat);
       maxk = max(maxk, L);  // the last tile's last row sees all L keys
     }
@@ -269,7 +277,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     vn = qsl[pe] - vq0;
     pref = viol == 0 && vn > 0;
     if (pref) {
-      tiles_v = (vn * G + RT - 1) / RT;
+      tiles_v = geo2.tiles(vn * G);  // the prefix sequence always runs on 256-row tiles
       if (p.forced_partition > 0) {
         Pv = P;
       } else {
@@ -294,7 +302,8 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const int s = rec.x, t = rec.y;
     seq(s, n, L);
     const int rows = n * G;
-    rows_t = min(RT, rows - t * RT);
+    const TileGeom geo = geom(rows);
+    rows_t = min(geo.RT, rows - t * geo.RT);
     km = geo.kmax(L, n, rows, t);
     const bool member = pref && s >= pb && s < pe;
     k0 = member ? ptok : 0;
@@ -380,13 +389,14 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     int len, k0, np_own, rows_t, km;
     const int np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km);
     const int pr = rec.z;
-    int4 sq;  // the sequence's first query token, query tokens and context
+    int4 sq;  // the sequence's first query token, query tokens and context, and its tile kind
     if (rec.x < kSeqCache) {
       const int4 c = seqc[rec.x];
-      sq = make_int4(c.w, c.x, c.y, 0);
+      sq = make_int4(c.w, c.x, c.y, tile_kind_for(c.x * G, p.tile_kind));
     } else {
       const int lo = qsl[rec.x];
-      sq = make_int4(lo, qsl[rec.x + 1] - lo, ctx[rec.x], 0);
+      const int n = qsl[rec.x + 1] - lo;
+      sq = make_int4(lo, n, ctx[rec.x], tile_kind_for(n * G, p.tile_kind));
     }
     for (int pp = 0; pp < np_own; ++pp) {
       const int kb = k0 + pp * len;
@@ -408,7 +418,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const int k = (i - tv * npv) * Pv;
     const int slot = atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
     p.buf.units[2 * slot] = make_int4(N, tv, k, -1);
-    p.buf.units[2 * slot + 1] = make_int4(vq0, vn, ptok - 1 + vn, 0);
+    p.buf.units[2 * slot + 1] = make_int4(vq0, vn, ptok - 1 + vn, 2);
   }
   if (tid == 0) {
     p.buf.hdr[kHdrUnits] = units_total;
@@ -475,7 +485,7 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
   const int q0 = p.query_start_loc[s];
   const int n = p.query_start_loc[s + 1] - q0;
   const int G = p.group;
-  const int RT = p.rows_per_tile;
+  const int RT = tile_rows_of(tile_kind_for(n * G, p.tile_kind));
   const int row0 = tile * RT;
   const int rows_here = min(RT, n * G - row0);
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -526,10 +536,11 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
 
 hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream) {
   if (tile_cap <= 0) return hipSuccess;
-  // One workgroup per (tile, kv head, quarter of the tile's row groups): most tiles are not split and their
-  // workgroups return at once, so the grid is kept small rather than one workgroup per row group.
+  // One workgroup per (tile, kv head, quarter of a 128-row tile's row groups; a 256-row tile's workgroups
+  // take twice the rows): most tiles are not split and their workgroups return at once, so the grid is kept
+  // small rather than one workgroup per row group.
   const int rows_per_wg = kThreads / (head_dim / 4);
-  const int z = (p.rows_per_tile + 4 * rows_per_wg - 1) / (4 * rows_per_wg);
+  const int z = (tile_rows_of(1) + 4 * rows_per_wg - 1) / (4 * rows_per_wg);
   const dim3 grid(static_cast<unsigned>(tile_cap), static_cast<unsigned>(p.num_kv_heads), static_cast<unsigned>(z));
   if (head_dim == 128) {
     hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(kThreads), 0, stream, p);

@@ -1,10 +1,11 @@
 // Paged attention for long query chunks, bf16 in / fp32 accumulate, on gfx950 MFMA.
 //
-// Same computation as the 16-row kernel (attention_bf16.hip): per sequence s and kv head g, the sequence's
+// Same computation as the 16-row item body (attention_narrow.h): per sequence s and kv head g, the sequence's
 // K/V are the first L rows of its physical blocks in block-table order ("Paged Attention 基础 – 原理与实现
 // 进度", §2 block-table figure, steps 1-4), and each new query token i (the last n positions) attends keys
 // 0 .. L-n+i with softmax(Q K^T * scale) V (same figure, step 5).  Used for row tiles of 256 (query token,
-// grouped head) rows, i.e. prefill and chunked-prefill work.
+// grouped head) rows, i.e. prefill and chunked-prefill work, and for the shared-prefix sequence of
+// paged_attention_forward_prefix.  attention.hip runs this item body and the 16-row one in one kernel.
 //
 // How (gfx950 design):
 //  * Each wave owns 32 rows of the tile per 32 x 32 half (v_mfma_f32_32x32x16_bf16, twice the sustained
@@ -25,6 +26,8 @@
 //    vector phases stagger instead of coinciding after every stage barrier.
 //  * Tiles with few rows (decode-like units of a mixed batch) split the keys among the waves, whose states
 //    are merged through LDS; split partitions write (acc, m, l) for split_reduce_kernel.
+#pragma once
+
 #include <type_traits>
 
 #include "device_util.h"
@@ -75,12 +78,13 @@ struct WideGeo {
   static_assert(NL >= 1 && KPW % KPL == 0, "stage split");
 };
 
-template <int D, int NH>
-__global__ void __launch_bounds__(64 * (8 / NH)) __attribute__((amdgpu_waves_per_eu(3 - NH, 3 - NH)))
-attn_wide_kernel(const AttnParams p) {
+// One work item (unit, kv head g) on 32-row waves.  Every thread of the workgroup calls it; `smem` is the
+// workgroup's ring (at least WideGeo<D, NH>::SMEM bytes of LDS); thread 0 claims the next item into
+// `next_item` once the item's last stage is consumed.
+template <int D, int NH = 1>
+__device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& pw, unsigned char* smem,
+                                          int unit, int g, int& next_item) {
   using T = WideGeo<D, NH>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::SMEM];
-  __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,13 +94,12 @@ attn_wide_kernel(const AttnParams p) {
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
   const int Hq = p.num_q_heads;
-  const int total_items = p.buf.hdr[kHdrUnits] * Hkv;
-  const int P = p.buf.hdr[kHdrPartition];
-  const int Pw = p.buf.hdr[kHdrPartitionWide];
+  const int P = pw.P;
+  const int Pw = pw.Pw;
   // Shared-prefix sequence (index num_seqs in the unit records; absent when it has no tokens).
-  const int pre_keys = p.buf.hdr[kHdrPrefKeys];
-  const int pre_table = p.buf.hdr[kHdrPrefTable];
-  const int pre_P = p.buf.hdr[kHdrPrefPartition];
+  const int pre_keys = pw.pre_keys;
+  const int pre_table = pw.pre_table;
+  const int pre_P = pw.pre_P;
   const int bs_log2 = p.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int last_block = static_cast<int>(p.num_blocks - 1);
@@ -130,22 +133,10 @@ attn_wide_kernel(const AttnParams p) {
 
   // Waves w and w + 4 share a SIMD.  Giving the lower one a higher issue priority lets its QK MFMAs run
   // first after each stage barrier, so that its softmax overlaps the partner's QK and its PV the partner's
-  // softmax, instead of both waves reaching their vector phases together.
+  // softmax, instead of both waves reaching their vector phases together.  (Reset when the item ends.)
   if (T::NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(1);
 
-  // The next item is claimed while the current one finishes, so the atomic's latency hides behind the
-  // epilogue.
-  int next_item = 0;
-  if (tid == 0) next_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
-  for (;;) {
-    if (tid == 0) s_item = next_item;
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
-    __syncthreads();
-    if (item >= total_items) break;
-
-    const int unit = item / Hkv;
-    const int g = item - unit * Hkv;
+  {
     // Unit record through scalar loads: {sequence, tile, first key, first partial row} and the sequence's
     // {first query token, query tokens, context}.
     const CONST_AS int* const urec = (const CONST_AS int*)p.buf.units + 8 * unit;
@@ -472,27 +463,8 @@ attn_wide_kernel(const AttnParams p) {
       }
     }
   }
+  if (T::NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(0);
 }
 
 }  // namespace
-
-int attention_wide_wgs_per_cu(int head_dim) {
-  // Eight waves (two per SIMD) or four waves with the whole register file: one workgroup per CU either
-  // way for D = 128 (its ring alone is 128 KiB); D = 64 fits two when the waves leave room.
-  using G128 = WideGeo<128, kWideHalves>;
-  using G64 = WideGeo<64, kWideHalves>;
-  static_assert(G128::SMEM + 64 <= 160 * 1024 && G64::SMEM + 64 <= 160 * 1024, "LDS");
-  if (kWideHalves == 2) return 1;
-  const int lds = (head_dim == 128 ? G128::SMEM : G64::SMEM) + 64;
-  const int wgs = (160 * 1024) / lds;
-  return wgs < 1 ? 1 : (wgs > 2 ? 2 : wgs);
-}
-
-hipError_t launch_attention_wide(const AttnParams& p, int head_dim, int grid, hipStream_t stream) {
-  const dim3 g(static_cast<unsigned>(grid)), b(WideGeo<128, kWideHalves>::THREADS);
-  if (head_dim == 128) hipLaunchKernelGGL((attn_wide_kernel<128, kWideHalves>), g, b, 0, stream, p);
-  else hipLaunchKernelGGL((attn_wide_kernel<64, kWideHalves>), g, b, 0, stream, p);
-  return hipGetLastError();
-}
-
 }  // namespace pkv

@@ -84,26 +84,20 @@ int check_pool(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_
 
 struct WsLayout {
   size_t hdr, seq_tiles, tile_rec, units, part_ml, part_acc, tok_info, total;
-  int rows_per_tile;
   int64_t tile_cap, unit_cap, prow_cap;
 };
 
-// Tile kind 1 (128-row tiles) when the hint says every sequence's rows (q_len x group) fit one such
-// tile; otherwise (long query chunks, or no hint) kind 2 (256-row tiles).  Only speed depends on it.
-int choose_tile_kind(int group, int64_t total_q, int32_t max_q_len_hint) {
-  if (g_tile_kind > 0) return g_tile_kind;
-  (void)total_q;
-  return (max_q_len_hint > 0 && static_cast<int64_t>(max_q_len_hint) * group <= pkv::tile_rows_of(1)) ? 1 : 2;
-}
-
+// The device picks each sequence's row tile (128 or 256 rows, pkv::tile_kind_for), so the layout bounds the
+// tile count with the shorter one: ceil(rows / 128) per sequence at most.  tile_kind 2 (forced) gives the
+// tighter bound of 256-row tiles.
 WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int tile_kind, int64_t partial_rows = pkv::kPartialRowCap) {
   WsLayout w{};
   w.prow_cap = partial_rows;
   const int group = num_q_heads / num_kv_heads;
-  w.rows_per_tile = pkv::tile_rows_of(tile_kind);
+  const int64_t rt = pkv::tile_rows_of(tile_kind == 2 ? 2 : 1);
   // Each sequence adds at most one partly filled tile.
-  w.tile_cap = (total_q * group + w.rows_per_tile - 1) / w.rows_per_tile + num_seqs;
+  w.tile_cap = (total_q * group + rt - 1) / rt + num_seqs;
   // Room for the items, one unit per tile when nothing is split, and a shared-prefix pass (at most about
   // 256 items plus one per prefix tile).
   w.unit_cap = (pkv::kMaxItems + num_kv_heads - 1) / num_kv_heads + 2 * w.tile_cap + 256;
@@ -253,11 +247,9 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int64_t total_q, int32_t
     return 0;
   }
   g_error.clear();
+  (void)max_q_len_hint;  // accepted for callers that have it; the device sizes each sequence's tiles itself
   if (dtype == PKV_FP32 || num_seqs == 0 || total_q == 0) return 0;
-  const int group = num_q_heads / num_kv_heads;
-  return workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
-                          choose_tile_kind(group, total_q, max_q_len_hint))
-      .total;
+  return workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, g_tile_kind).total;
 }
 
 }  // extern "C"
@@ -323,7 +315,14 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
     return succeed();
   }
 
-  const int tile_kind = prefix ? 2 : choose_tile_kind(group, total_q, max_q_len_hint);
+  // Each sequence's tile kind is chosen on the device from its own q_len, unless tuning forces one.  A
+  // q-length bound that puts every sequence's rows in one 128-row tile lets the call plan 128-row tiles
+  // throughout and run the kernel build with only the 16-row body (a wrong bound only costs speed: longer
+  // sequences then take several 128-row tiles).
+  const bool narrow_only = g_tile_kind == 1 ||
+                           (g_tile_kind == 0 && !prefix && max_q_len_hint > 0 &&
+                            static_cast<int64_t>(max_q_len_hint) * group <= pkv::tile_rows_of(1));
+  const int tile_kind = narrow_only ? 1 : g_tile_kind;
   WsLayout w = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind);
   if (noalloc) {
     // The library's scratch: the per-call records must fit; the rest holds as many partial rows as it
@@ -355,7 +354,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   b.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
   b.tok_info = reinterpret_cast<int4*>(ws + w.tok_info);
   p.buf = b;
-  p.rows_per_tile = w.rows_per_tile;
+  p.tile_kind = tile_kind;
 
   pkv::PlanParams pp{};
   pp.context_lens = context_lens;
@@ -364,12 +363,12 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   pp.total_q = total_q;
   pp.group = group;
   pp.num_kv_heads = num_kv_heads;
-  pp.rows_per_tile = w.rows_per_tile;
+  pp.tile_kind = tile_kind;
   pp.max_context = max_blocks_per_seq * block_size;
   int items = g_target_items > 0 ? g_target_items : pkv::kDefaultItems;
   if (items > pkv::kMaxItems) items = pkv::kMaxItems;
   pp.target_items = items;
-  const int64_t grid_wgs = static_cast<int64_t>(num_cus()) * pkv::attention_bf16_wgs_per_cu(head_dim, tile_kind);
+  const int64_t grid_wgs = static_cast<int64_t>(num_cus()) * pkv::attention_wgs_per_cu(head_dim, narrow_only);
   pp.min_items = g_target_items > 0 ? 0 : static_cast<int>(2 * grid_wgs);
   pp.forced_partition = g_partition_keys;
   pp.unit_cap = static_cast<int>(w.unit_cap);
@@ -386,7 +385,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   const int64_t max_items = w.unit_cap * num_kv_heads;
   if (grid > max_items) grid = max_items;
   if (timed) hipEventRecord(g_ev_start, st);
-  e = pkv::launch_attention_bf16(p, head_dim, tile_kind, static_cast<int>(grid), st);
+  e = pkv::launch_attention(p, head_dim, narrow_only, static_cast<int>(grid), st);
   if (e != hipSuccess) return hip_fail("attention launch", e);
   if (timed) hipEventRecord(g_ev_stop, st);
   e = pkv::launch_split_reduce(p, head_dim, static_cast<int>(w.tile_cap), st);
@@ -435,7 +434,7 @@ size_t paged_attention_prefix_workspace_size(int32_t num_seqs, int64_t total_q, 
   }
   g_error.clear();
   if (dtype == PKV_FP32 || num_seqs == 0 || total_q == 0) return 0;
-  return workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, 2).total;
+  return workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, g_tile_kind).total;
 }
 
 int paged_attention_forward_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -14,13 +14,18 @@ constexpr int kThreads = 256;
 // 32-bit index, so a call may move at most INT32_MAX - kWriteGridLanes chunks.
 constexpr int kWriteMaxBlocks = 8192;
 constexpr int kWriteGridLanes = kWriteMaxBlocks * kThreads;
-// Row-tile kinds of the bf16 attention.  Kind 1: 128-row tiles, 8 waves of 16 rows (two waves per SIMD),
-// for rows-poor batches (decode, speculative decode).  Kind 2: 256-row tiles, 8 waves of 32 rows (two
-// waves per SIMD, 32 x 32 MFMA tiles), for long query chunks.
+// Row-tile kinds of the bf16 attention, chosen per sequence by the planner.  Kind 1: 128-row tiles, 8 waves
+// of 16 rows (two waves per SIMD), for sequences whose q_len x group rows fit one tile (decode, speculative
+// decode).  Kind 2: 256-row tiles, 8 waves of 32 rows (two waves per SIMD, 32 x 32 MFMA tiles), for long
+// query chunks.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int tile_rows_of(int kind) { return kind == 1 ? 128 : 256; }
 constexpr int kMaxTileRows = tile_rows_of(2);
+// Tile kind of a sequence with `rows` = q_len x group rows per kv head; `forced` (1 or 2) overrides it.
+__host__ __device__ inline int tile_kind_for(int rows, int forced) {
+  return forced > 0 ? forced : (rows <= tile_rows_of(1) ? 1 : 2);
+}
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
 constexpr int kDefaultItems = 1024;
@@ -62,8 +67,8 @@ struct PlanBuffers {
   int* seq_tiles;   // [num_seqs]  scratch
   int4* tile_rec;   // [tile_cap]  {sequence, tile, first partial row or -1, number of partitions}
   // [unit_cap][2]: {sequence, tile, first key of the partition, first partial row or -1 if unsplit}, then the
-  // sequence's {first query token, query tokens, context length, 0}, so that an item needs no further
-  // dependent metadata load
+  // sequence's {first query token, query tokens, context length} and the tile kind (1 or 2), so that an item
+  // needs no further dependent metadata load
   int4* units;
   float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
   float* part_acc;  // [prow_cap * head_dim] unnormalised partial outputs
@@ -94,7 +99,7 @@ struct PlanParams {
   int64_t total_q;
   int group;          // num_q_heads / num_kv_heads
   int num_kv_heads;
-  int rows_per_tile;
+  int tile_kind;      // 0: per sequence (tile_kind_for); 1 or 2: every sequence
   int max_context;    // max_blocks_per_seq * block_size: longer contexts are rejected on the device
   int target_items;
   int min_items;      // 0, or the item count that partitions may not be lengthened below (see kSoftMinPartition)
@@ -125,13 +130,19 @@ struct AttnParams {
   int num_kv_heads;
   int group;
   int block_size_log2;
-  int rows_per_tile;
+  int tile_kind;         // as PlanParams::tile_kind (the split reduce recovers each tile's height from it)
   int64_t num_blocks;
   int64_t block_stride;  // elements
   int64_t total_q;
   float scale;           // natural-exponent scale
   float scale_log2;      // scale * log2(e)
   PlanBuffers buf;
+};
+
+// Words of the plan header every work item needs, read once per workgroup (scalar loads) before the first
+// item: partition lengths, and the shared-prefix sequence's key count, table row and partition length.
+struct PlanWords {
+  int P, Pw, pre_keys, pre_table, pre_P;
 };
 
 struct KvWriteParams {
@@ -160,14 +171,12 @@ struct CopyBlocksParams {
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, int num_pairs, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
-// grid = persistent workgroups; tile_kind 1 runs the 16-row kernel, 2 the 64-row (wide) one.
-hipError_t launch_attention_bf16(const AttnParams& p, int head_dim, int tile_kind, int grid,
-                                 hipStream_t stream);
-hipError_t launch_attention_wide(const AttnParams& p, int head_dim, int grid, hipStream_t stream);
-int attention_wide_wgs_per_cu(int head_dim);
+// grid = persistent workgroups; each work item runs on the tile kind its unit carries, or (narrow_only) on the
+// 16-row body, for plans made with tile kind 1 throughout.
+hipError_t launch_attention(const AttnParams& p, int head_dim, bool narrow_only, int grid, hipStream_t stream);
 hipError_t launch_split_reduce(const AttnParams& p, int head_dim, int tile_cap, hipStream_t stream);
 hipError_t launch_attention_fp32(const AttnParams& p, int head_dim, hipStream_t stream);
 // Workgroups per CU the bf16 attention kernel is built for (from its LDS footprint).
-int attention_bf16_wgs_per_cu(int head_dim, int tile_kind);
+int attention_wgs_per_cu(int head_dim, bool narrow_only);
 
 }  // namespace pkv

@@ -390,3 +390,21 @@ def test_rejected_sequences_give_nan_rows(dtype, kind):
     _, _, ref = oracle.run_step(w.k_pool, w.v_pool, w.block_tables, w.steps[0], w.scale, w.dtype, seqs=[0, 2])
     good = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in (0, 2)])
     check_close(got[good], ref[good], dtype, "valid sequences beside rejected ones")
+
+
+@pytest.mark.parametrize("hint", [None, 1, 4096])
+@pytest.mark.parametrize("name", ["mixed", "decode", "spec"])
+def test_q_length_hint_only_changes_speed(name, hint):
+    """The q-length hint only picks a kernel build: no hint (each sequence's tile kind chosen on the device),
+    a hint too small for the batch (128-row tiles for every sequence, long chunks over several of them), or a
+    loose one all give the oracle's result."""
+    w = make_config(name, "small")
+    log(f"small {name}, q-length hint {hint}")
+    dw = DeviceWorkload(w)
+    s = dw.steps[0]
+    pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], dw.k_pool, dw.v_pool)
+    out = pkv.paged_attention_forward(s["q"], dw.k_pool, dw.v_pool, dw.block_tables, s["context_lens"],
+                                      s["query_start_loc"], scale=w.scale, max_q_len=hint)
+    torch.cuda.synchronize()
+    _, _, outs = _oracle_steps(w)
+    check_close(out_f64(out), outs[0], BF16, f"{name} hint={hint}")
