@@ -28,7 +28,7 @@ __host__ __device__ inline int tile_kind_for(int rows, int forced) {
 }
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
-constexpr int kDefaultItems = 1024;
+constexpr int kDefaultItems = 768;
 constexpr int kMinPartition = 256;
 // With the automatic item target, partitions are lengthened up to this many keys as long as the call
 // keeps PlanParams::min_items items: every item costs a pipeline fill and an epilogue, so fewer, longer
