@@ -164,9 +164,20 @@ def _attention_args(q, k_cache, v_cache, block_tables, context_lens, query_start
     return dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, float(scale)
 
 
+# Workspaces the binding owns for callers that pass none: one per (device, stream), grown when a call needs
+# more and reused otherwise.  Calls on one stream are ordered, so they can share it; calls on different
+# streams get different ones.
+_WORKSPACES: dict = {}
+
+
 def _workspace(workspace, need, dev):
     if workspace is None:
-        return torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+        ws = _WORKSPACES.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            _WORKSPACES[key] = ws
+        return ws
     if workspace.device != dev or workspace.dtype != torch.uint8:
         raise ValueError("workspace must be a uint8 tensor on q's device")
     return workspace
@@ -181,7 +192,9 @@ def paged_attention_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
 
     ``q`` ``[total_q, H_q, D]`` packs each sequence's new tokens at ``query_start_loc[s] :
     query_start_loc[s+1]``; ``context_lens[s]`` counts every cached token including them.  ``scale``
-    defaults to ``1/sqrt(D)``.  ``workspace`` (uint8, device) is allocated when not given.  Returns
+    defaults to ``1/sqrt(D)``.  ``workspace`` (uint8, device): when not given, the binding's own workspace for
+    this device and stream (allocated once, grown when a call needs more).  ``max_q_len`` (optional, an upper
+    bound on q_len) lets decode-like batches run the kernel build with only the 16-row body.  Returns
     ``out`` ``[total_q, H_q, D]`` in q's dtype.  Asynchronous on the current stream."""
     dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, scale = _attention_args(
         q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, validate)

@@ -256,6 +256,16 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     if (p.min_items > 0) {
       const long long soft = min(static_cast<long long>(kSoftMinPartition), items / p.min_items / kStageKeys * kStageKeys);
       P = max(P, static_cast<int>(min(soft, static_cast<long long>(pmax))));
+      // No split at all when the unsplit tiles already give each workgroup of the grid (min_items / 2) at
+      // most one item and the longest is within kNoSplitSlack of the per-workgroup average: the makespan is
+      // then that longest item, while splitting would add fills, partial rows and their merge to every
+      // workgroup (measured: 256 MQA decodes over 2K-3K keys take 52 us unsplit vs 60 us split).  Spread
+      // lengths or more items than workgroups are better balanced by partitions (decode batches, long
+      // speculative contexts).  Not used with the shared-prefix pass, which partitions its own way.
+      const long long grid = p.min_items / 2;
+      if (p.prefix.tokens <= 0 && static_cast<long long>(total_tiles) * Hkv <= grid &&
+          static_cast<long long>(max_kmax) * grid * kNoSplitSlackDen <= kNoSplitSlackNum * total_work * Hkv)
+        P = pmax;
     }
   }
   auto wide_len = [&](int P_) { return p.forced_partition > 0 ? P_ : min(max(P_, kWidePartitionMin), pmax); };

@@ -34,6 +34,10 @@ constexpr int kMinPartition = 256;
 // keeps PlanParams::min_items items: every item costs a pipeline fill and an epilogue, so fewer, longer
 // items are faster while there are enough of them to balance the grid.
 constexpr int kSoftMinPartition = 2048;
+// A call is left unsplit when its unsplit items number at most one per workgroup and the longest context is at
+// most kNoSplitSlackNum / kNoSplitSlackDen times the average work per workgroup.
+constexpr int kNoSplitSlackNum = 13;
+constexpr int kNoSplitSlackDen = 10;
 
 // Workspace header words.
 enum HeaderWord {

@@ -408,3 +408,30 @@ def test_q_length_hint_only_changes_speed(name, hint):
     torch.cuda.synchronize()
     _, _, outs = _oracle_steps(w)
     check_close(out_f64(out), outs[0], BF16, f"{name} hint={hint}")
+
+
+def test_equal_contexts_one_item_per_workgroup_stay_unsplit():
+    """As many single-token MQA sequences as the GPU has CUs (one workgroup each), with contexts within 10% of
+    each other: the automatic plan leaves every context unsplit (partition length >= the longest context) and
+    the result matches the oracle; the same count with contexts spread over 500-4000 keys is split."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for lo, hi, expect_unsplit in ((1900, 2100, True), (500, 4000, False)):
+        n_seqs = cus
+        rng = np.random.default_rng(53 + lo)
+        ctx = rng.integers(lo, hi, n_seqs)
+        w = build_workload(rng, name="even", dtype=BF16, num_q_heads=32, num_kv_heads=1, head_dim=128,
+                           block_size=16, q_lens=[1] * n_seqs, context_lens=ctx)
+        log(f"{n_seqs} MQA decodes, contexts {lo}-{hi}, on {cus} CUs")
+        dw = DeviceWorkload(w)
+        st = dw.steps[0]
+        ws = torch.zeros(max(256, pkv.workspace_size(w.num_seqs, st["q"].shape[0], w.num_q_heads,
+                                                     w.num_kv_heads, w.head_dim, st["q"].dtype, 1)),
+                         dtype=torch.uint8, device=st["q"].device)
+        pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], dw.k_pool, dw.v_pool)
+        out = pkv.paged_attention_forward(st["q"], dw.k_pool, dw.v_pool, dw.block_tables, st["context_lens"],
+                                          st["query_start_loc"], scale=w.scale, workspace=ws, max_q_len=1)
+        torch.cuda.synchronize()
+        partition = int(ws[:64].cpu().numpy().view(np.int32)[2])
+        assert (partition >= int(ctx.max())) == expect_unsplit, (n_seqs, partition, int(ctx.max()))
+        _, _, outs = _oracle_steps(w)
+        check_close(out_f64(out), outs[0], BF16, f"{n_seqs} MQA decodes, contexts {lo}-{hi}")
