@@ -33,7 +33,8 @@ struct AttnSmem {
 // separately because the 16-row body alone needs far fewer registers (about 160) than the two bodies
 // together, and decode-like batches, which only ever need it, run measurably faster without the other.
 template <int D, bool NARROW_ONLY>
-__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kAttnThreads)
+__attribute__((amdgpu_waves_per_eu(kAttnWavesPerSimd, kAttnWavesPerSimd)))
 attn_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16)))
   unsigned char smem[NARROW_ONLY ? Geo<D, 1>::SMEM : AttnSmem<D>::BYTES];
@@ -73,11 +74,16 @@ attn_kernel(const AttnParams p) {
 }  // namespace
 
 int attention_wgs_per_cu(int head_dim, bool narrow_only) {
-  // 160 KiB of LDS per CU; a workgroup holds the 4-stage K/V ring (reused for the merges) plus a word.
+  // Registers: kAttnWavesPerSimd waves per SIMD.  LDS: 160 KiB per CU; a workgroup holds the 4-stage K/V
+  // ring (reused for the merges) plus a word.  (The runtime's occupancy query counts only the
+  // architectural registers, and overstates this for builds that also use accumulation registers.)
+  constexpr int by_regs = kAttnWavesPerSimd * 4 / kAttnWaves;
+  static_assert(by_regs >= 1, "a workgroup fits a CU");
   const int smem = narrow_only ? (head_dim == 128 ? Geo<128, 1>::SMEM : Geo<64, 1>::SMEM)
                                : (head_dim == 128 ? AttnSmem<128>::BYTES : AttnSmem<64>::BYTES);
-  const int wgs = (160 * 1024) / (smem + 64);
-  return wgs < 1 ? 1 : (wgs > 2 ? 2 : wgs);
+  const int by_lds = (160 * 1024) / (smem + 64);
+  const int wgs = by_lds < by_regs ? by_lds : by_regs;
+  return wgs < 1 ? 1 : wgs;
 }
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, bool narrow_only, int grid, hipStream_t stream) {

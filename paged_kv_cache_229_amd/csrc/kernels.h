@@ -20,6 +20,10 @@ constexpr int kWriteGridLanes = kWriteMaxBlocks * kThreads;
 // query chunks.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
+// The attention kernels are compiled for exactly this many waves per SIMD (amdgpu_waves_per_eu), so the
+// compiler may give each wave up to 512 / kAttnWavesPerSimd registers (every build takes more than 128,
+// counting accumulation registers): kAttnWavesPerSimd * 4 SIMDs / kAttnWaves workgroups fit on a CU.
+constexpr int kAttnWavesPerSimd = 2;
 constexpr int tile_rows_of(int kind) { return kind == 1 ? 128 : 256; }
 constexpr int kMaxTileRows = tile_rows_of(2);
 // Tile kind of a sequence with `rows` = q_len x group rows per kv head; `forced` (1 or 2) overrides it.
