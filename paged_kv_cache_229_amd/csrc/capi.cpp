@@ -318,10 +318,11 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   // Each sequence's tile kind is chosen on the device from its own q_len, unless tuning forces one.  A
   // q-length bound that puts every sequence's rows in one 128-row tile lets the call plan 128-row tiles
   // throughout and run the kernel build with only the 16-row body (a wrong bound only costs speed: longer
-  // sequences then take several 128-row tiles).
-  const bool narrow_only = g_tile_kind == 1 ||
-                           (g_tile_kind == 0 && !prefix && max_q_len_hint > 0 &&
-                            static_cast<int64_t>(max_q_len_hint) * group <= pkv::tile_rows_of(1));
+  // sequences then take several 128-row tiles).  A call with a shared-prefix pass always runs the build with
+  // both bodies: the prefix sequence's units are 256-row tiles whatever the members' kind.
+  const bool narrow_only = !prefix && (g_tile_kind == 1 ||
+                                       (g_tile_kind == 0 && max_q_len_hint > 0 &&
+                                        static_cast<int64_t>(max_q_len_hint) * group <= pkv::tile_rows_of(1)));
   const int tile_kind = narrow_only ? 1 : g_tile_kind;
   WsLayout w = workspace_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, tile_kind);
   if (noalloc) {

@@ -31,7 +31,7 @@ def share(tables, begin, end, blocks):
 PLAN_PREFIX_TOKENS_WORD = 7
 
 
-def run_prefix(w, tables, begin, end, prefix_tokens, what, partition=0, active=True):
+def run_prefix(w, tables, begin, end, prefix_tokens, what, partition=0, active=True, kind=0):
     st = w.steps[0]
     kp, vp = to_torch(w.k_pool, w.dtype), to_torch(w.v_pool, w.dtype)
     bt = to_torch(tables, None)
@@ -39,7 +39,7 @@ def run_prefix(w, tables, begin, end, prefix_tokens, what, partition=0, active=T
     log(f"prefix pass: {what}")
     pkv.paged_kv_write(to_torch(st.k_new, w.dtype), to_torch(st.v_new, w.dtype),
                        to_torch(st.slot_mapping, None), kp, vp)
-    pkv.set_tuning(partition, 0, 0)
+    pkv.set_tuning(partition, 0, kind)
     try:
         need = pkv.prefix_workspace_size(w.num_seqs, q.shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim,
                                          q.dtype)
@@ -76,6 +76,16 @@ def test_subrange_with_spec_members(partition):
     ctx = [500, 300, 700, 260, 900, 300, 40, 800]
     w = custom(1, q_lens, ctx)
     run_prefix(w, share(w.block_tables, 1, 6, 16), 1, 6, 256, f"sub-range, partition {partition}", partition)
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_forced_tile_kind(kind):
+    """A forced row-tile kind applies to the members' own tiles; the prefix sequence keeps its 256-row
+    tiles, so the call runs the kernel build with both bodies."""
+    q_lens = [3, 1, 4, 2, 1, 4, 1, 2]
+    ctx = [500, 300, 700, 260, 900, 300, 40, 800]
+    w = custom(11, q_lens, ctx)
+    run_prefix(w, share(w.block_tables, 1, 6, 16), 1, 6, 256, f"forced tile kind {kind}", kind=kind)
 
 
 def test_head_dim_64_and_mqa():
