@@ -135,8 +135,10 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
                    : rows_here <= 2 * T::WROWS ? 2
                    : rows_here <= 4 * T::WROWS ? 4 : 8;
     const int WK = T::NW / WR;
-    const int wr = wave / WK;
-    const int wk = wave - wr * WK;
+    // Wave w (on SIMD w % 4) takes row group w % WR and key group w / WR: the waves that compute one stage's
+    // chunks (two key groups, all row groups) then sit on different SIMDs.
+    const int wk = wave / WR;
+    const int wr = wave - wk * WR;
     const int my_row0 = row0 + wr * T::WROWS;
     // 16-row n-tiles of this wave that hold rows of the item (0 when the last row group is empty).
     const int ntv = min(NTW, (row0 + rows_here - my_row0 + 15) >> 4);
