@@ -60,11 +60,14 @@ struct TileGeom {
   }
 };
 
-// Stage-count bucket of a unit, longest first.
-__device__ inline int sort_bucket(int keys) {
-  const int stages = (keys + kStageKeys - 1) / kStageKeys;
+// Stage-count bucket of a unit, longest first.  A stage of a 256-row tile (32-row waves, bound by the matrix
+// cores) takes about twice as long as a stage of a 128-row tile (16-row waves, bound by the copies), so the
+// former count double (weight 2): units are ordered by estimated time, not key count.
+__device__ inline int sort_bucket(int keys, int weight) {
+  const int stages = weight * ((keys + kStageKeys - 1) / kStageKeys);
   return kSortBuckets - 1 - min(stages, kSortBuckets - 1);
 }
+__device__ inline int kind_weight(int kind) { return kind == 2 ? 2 : 1; }
 
 // Wave-wide inclusive prefix sum with DPP lane moves (no LDS traffic): running sums within each row of 16
 // lanes by shifts of 1, 2, 4 and 8, then row 0's total into row 1 and row 2's into row 3 (row_bcast:15),
@@ -291,8 +294,12 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       if (p.forced_partition > 0) {
         Pv = P;
       } else {
-        // about one prefix item per CU, partitions of at least 256 keys
-        const int want = min(max(1, (256 + tiles_v * Hkv - 1) / (tiles_v * Hkv)), max(1, ptok / 256));
+        // About one prefix item per two workgroups of the attention grid (min_items / 2 workgroups; a stage of
+        // these 256-row tiles takes about twice as long as one of the members' 128-row tiles), partitions of
+        // at least 256 keys.  Measured on 256 members over a 2048-key prefix (32 tiles): 3-4 partitions per
+        // tile give 36-37 us of kernel time, 8 partitions 42 us (and twice the partial rows), 2 partitions 46 us.
+        const int pre_items = p.min_items > 0 ? max(1, p.min_items / 4) : 128;
+        const int want = min(max(1, (pre_items + tiles_v * Hkv - 1) / (tiles_v * Hkv)), max(1, ptok / 256));
         Pv = ((ptok + want - 1) / want + kStageKeys - 1) / kStageKeys * kStageKeys;
       }
       npv = (ptok + Pv - 1) / Pv;
@@ -307,12 +314,13 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   // (after the prefix for members of the shared-prefix pass) and has *np_own partitions of *len keys;
   // returns all partitions of the tile including the prefix ones.  Also gives the tile's rows and kmax.
   auto tile_parts = [&](const int4 rec, int P_, int Pw_, const FastDiv& dp, const FastDiv& dw, int& len, int& k0,
-                        int& np_own, int& rows_t, int& km) -> int {
+                        int& np_own, int& rows_t, int& km, int& wt) -> int {
     int n, L;
     const int s = rec.x, t = rec.y;
     seq(s, n, L);
     const int rows = n * G;
     const TileGeom geo = geom(rows);
+    wt = kind_weight(geo.kind);
     rows_t = min(geo.RT, rows - t * geo.RT);
     km = geo.kmax(L, n, rows, t);
     const bool member = pref && s >= pb && s < pe;
@@ -330,7 +338,8 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     int units = 0, prows = 0;
     for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
       int len, k0, np_own, rows_t, km;
-      const int np = tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km);
+      int wt;
+      const int np = tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
       units = min(units + np_own, kSat);
       if (np > 1) prows = min(prows + min(np * rows_t, kSat) * Hkv, kSat);
     }
@@ -352,7 +361,8 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       if (tau < total_tiles) {
         rec = p.buf.tile_rec[tau];
         int len, k0, np_own, rows_t, km;
-        np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km);
+        int wt;
+        np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
         if (np > 1) pr = np * rows_t * Hkv;
       }
       int sum;
@@ -368,12 +378,13 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   __syncthreads();
   for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
     int len, k0, np_own, rows_t, km;
-    tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km);
-    for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len))], 1);
+    int wt;
+    tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
+    for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len), wt)], 1);
   }
   for (int i = tid; i < units_v; i += kPlanThreads) {
     const int k = (i % npv) * Pv;
-    atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
+    atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv), kind_weight(2))], 1);
   }
   __syncthreads();
   {
@@ -397,7 +408,8 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
     const int4 rec = p.buf.tile_rec[tau];
     int len, k0, np_own, rows_t, km;
-    const int np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km);
+    int wt;
+    const int np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
     const int pr = rec.z;
     int4 sq;  // the sequence's first query token, query tokens and context, and its tile kind
     if (rec.x < kSeqCache) {
@@ -410,7 +422,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     }
     for (int pp = 0; pp < np_own; ++pp) {
       const int kb = k0 + pp * len;
-      const int slot = atomicAdd(&bucket[sort_bucket(min(km - kb, len))], 1);
+      const int slot = atomicAdd(&bucket[sort_bucket(min(km - kb, len), wt)], 1);
       p.buf.units[2 * slot] = make_int4(rec.x, rec.y, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
       p.buf.units[2 * slot + 1] = sq;
     }
@@ -426,7 +438,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   for (int i = tid; i < units_v; i += kPlanThreads) {
     const int tv = i / npv;
     const int k = (i - tv * npv) * Pv;
-    const int slot = atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv))], 1);
+    const int slot = atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv), kind_weight(2))], 1);
     p.buf.units[2 * slot] = make_int4(N, tv, k, -1);
     p.buf.units[2 * slot + 1] = make_int4(vq0, vn, ptok - 1 + vn, 2);
   }
