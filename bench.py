@@ -118,12 +118,14 @@ def _to_device(dev, a, is_data=True):
 
 
 def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, prefix_pass: bool = False,
-               graph: bool = False) -> dict:
+               graph: bool = False, reuse: bool = False) -> dict:
     """Warm up, then time exactly ``steps`` steps (paged_kv_write + paged_attention_forward of the workload's
     step, each on the next of ``copies`` pool copies) between two device synchronisations, with nothing else
     on the stream.  The same number of steps then runs again with events on the launch stream, for the
     attention kernel alone (HIP events the library records around it) and the whole attention call (plan +
-    attention + split reduce: torch events around the call)."""
+    attention + split reduce: torch events around the call).  reuse: the pool copies stand for the layers
+    of a model step, which share the metadata: the call on copy 0 plans (paged_attention_forward), the calls
+    on the other copies run on its plan (paged_attention_run)."""
     import numpy as np
     import torch
 
@@ -166,6 +168,9 @@ def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, pr
         if prefix_tokens:
             pkv.paged_attention_forward_prefix(q, kp, vp, bt, cl, qsl, 0, w.num_seqs, prefix_tokens,
                                                scale=w.scale, out=out, workspace=ws)
+        elif reuse and i % len(pools) != 0:
+            pkv.paged_attention_run(q, kp, vp, bt, cl, qsl, scale=w.scale, out=out, workspace=ws,
+                                    max_q_len=max_q)
         else:
             pkv.paged_attention_forward(q, kp, vp, bt, cl, qsl, scale=w.scale, out=out, workspace=ws,
                                         max_q_len=max_q)
@@ -255,6 +260,22 @@ def hbm_view(dev, name: str, steps: int, warmup: int, copies: int) -> dict:
             "traffic": recorded_traffic(w.name), "tokens_per_s": round(work["total_q"] / (t["ms_per_step"] * 1e-3), 1)}
 
 
+def plan_reuse_view(dev, name: str, steps: int, warmup: int, copies: int) -> dict:
+    """The workload's step as one layer of a model step whose layers share the metadata: every ``copies``-th
+    call plans (paged_attention_forward), the others run on that plan (paged_attention_run).  Per-layer wall
+    time and whole-call time, beside the plain step's."""
+    from workloads import make_config
+
+    w = make_config(name, "full")
+    work = algorithmic_work(w)
+    t = time_steps(dev, w, steps, warmup, copies, reuse=True)
+    sgbs = (work["attn_bytes_unique"] + work["write_bytes"]) / (t["ms_per_step"] * 1e-3) / 1e9
+    cgbs = work["attn_bytes_unique"] / (t["call_ms"] * 1e-3) / 1e9
+    return {"workload": w.name, "layers_per_plan": copies, "ms_per_layer": round(t["ms_per_step"], 4),
+            "layer_frac": round(sgbs / HBM_PEAK_GBS, 4), "attention_call_ms": t["call"],
+            "attention_call_frac": round(cgbs / HBM_PEAK_GBS, 4)}
+
+
 def prefill_view(dev, steps: int, warmup: int, copies: int) -> dict:
     """The other half of the metric: the chunked-prefill step's 8 prefill chunks alone (512 tokens each over a
     prior context U[0, 2048], the launch `--workload mixed --subset prefill` times), with the attention kernel
@@ -341,6 +362,9 @@ def main() -> None:
     ap.add_argument("--tile-kind", type=int, default=0)
     ap.add_argument("--subset", choices=["all", "prefill", "decode"], default="all",
                     help="time only the sequences with q_len > 1 (prefill) or q_len == 1 (decode)")
+    ap.add_argument("--plan-reuse", action="store_true",
+                    help="the pool copies are the layers of one model step: plan on the first, run the others "
+                         "on that plan (paged_attention_run)")
     ap.add_argument("--prefix-pass", action="store_true",
                     help="prefix workload: attend the shared blocks once for all sequences "
                          "(paged_attention_forward_prefix)")
@@ -386,6 +410,10 @@ def main() -> None:
         w.description += f" [{args.subset} sequences only: {len(keep)}]"
     print(f"[bench] generated {w.description} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
+    if args.plan_reuse and args.prefix_pass:
+        print("bench.py: --plan-reuse runs plain calls on a reused plan; it does not combine with --prefix-pass",
+              file=sys.stderr)
+        sys.exit(2)
     if args.prefix_pass and w.shared_prefix_blocks == 0:
         print("bench.py: --prefix-pass needs a workload with shared prefix blocks (prefix)", file=sys.stderr)
         sys.exit(2)
@@ -396,7 +424,7 @@ def main() -> None:
     kernel_name = kernel_name_for(w, args.tile_kind, args.prefix_pass)
     pkv.set_tuning(args.partition, args.items, args.tile_kind)  # the workspace size depends on it
     t = time_steps(dev, w, args.steps, args.warmup, args.copies, layers=args.layers,
-                   prefix_pass=args.prefix_pass, graph=args.graph)
+                   prefix_pass=args.prefix_pass, graph=args.graph, reuse=args.plan_reuse)
     print(f"[bench] headline timed: {t['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
 
     ms_step = t["ms_per_step"]
@@ -424,7 +452,8 @@ def main() -> None:
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "pool_copies": t["pool_copies"],
                    "pool_layout": "per_layer" if args.layers == 1 else f"layer_in_block x{args.layers}",
-                   "shared_prefix_pass": bool(args.prefix_pass), "launch": t["launch"]},
+                   "shared_prefix_pass": bool(args.prefix_pass), "plan_reuse": bool(args.plan_reuse),
+                   "launch": t["launch"]},
         "tokens_per_s": round(work["total_q"] / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attention_kernel_ms": t["kernel"],
@@ -449,7 +478,8 @@ def main() -> None:
     if work["prefill_flops"]:
         result["prefill_subset_flops"] = work["prefill_flops"]
     default_shape = (args.workload == "spec" and args.subset == "all" and args.layers == 1 and not args.graph
-                     and not args.prefix_pass and not (args.partition or args.items or args.tile_kind))
+                     and not args.prefix_pass and not args.plan_reuse
+                     and not (args.partition or args.items or args.tile_kind))
     if default_shape and not args.no_views:
         torch.cuda.empty_cache()
         result["decode_view"] = hbm_view(dev, "decode", args.steps, args.warmup, args.copies)
@@ -457,6 +487,10 @@ def main() -> None:
         torch.cuda.empty_cache()
         result["prefill_view"] = prefill_view(dev, args.steps, args.warmup, args.copies)
         print("[bench] prefill view timed", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        result["plan_reuse_view"] = [plan_reuse_view(dev, name, args.steps, args.warmup, args.copies)
+                                     for name in ("spec", "decode")]
+        print("[bench] plan-reuse views timed", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, work, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -125,8 +125,9 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int64_t total_q, int32_t
  *                 finite and > 0 (a softmax temperature), else PKV_ERR_INVALID_ARG
  *   max_q_len_hint  an upper bound on n over the batch, or <= 0 if unknown (picks the row tile)
  *   workspace     (device) scratch of at least paged_attention_workspace_size() bytes, 256-byte aligned;
- *                 its contents need no initialisation and are meaningless after the call.  Calls that
- *                 share one workspace must be ordered (same stream or synchronised).
+ *                 its contents need no initialisation; after the call it holds the call's work plan, which
+ *                 paged_attention_run may reuse.  Calls that share one workspace must be ordered (same
+ *                 stream or synchronised).
  * Accumulation is in float32; PKV_BF16 outputs are rounded to nearest even.  num_seqs == 0 or total_q
  * == 0 is a valid no-op.
  */
@@ -138,6 +139,31 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                             int64_t num_blocks, int64_t block_stride, float scale, int32_t dtype,
                             int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * paged_attention_run — paged_attention_forward on the work plan an earlier call left in `workspace`,
+ * without planning again.  Every layer of a model step calls attention with its own k_cache[i], v_cache[i]
+ * but the same block tables and lengths (ADR 004 "Paged Attention Serving Integration", Decision 4), and
+ * the plan -- how the batch is cut into work items and partial rows -- depends on nothing else: call
+ * paged_attention_forward for the step's first layer and paged_attention_run for the others, with the same
+ * workspace, the same block_tables / context_lens / query_start_loc (contents included), the same sizes,
+ * max_q_len_hint and tuning; out, q, k_cache, v_cache and scale may differ.  The result is then identical
+ * to paged_attention_forward's with the same arguments.
+ *  - Same arguments and errors as paged_attention_forward.
+ *  - The plan records the call's shape (sizes, row-tile kind, workspace layout).  If the workspace holds no
+ *    plan for this shape, nothing is computed and every output element is NaN.  The metadata's contents
+ *    are not checked: with contents other than the plan's, the output is undefined, but every access stays
+ *    inside the call's buffers and the workspace.
+ *  - Calls sharing the workspace must be ordered (same stream or synchronised); the plan is the one the
+ *    last paged_attention_forward or paged_attention_forward_prefix call on the workspace made.
+ * PKV_FP32 has no plan and runs as paged_attention_forward.
+ */
+int paged_attention_run(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        const int32_t* query_start_loc, int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                        int64_t block_stride, float scale, int32_t dtype, int32_t max_q_len_hint, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * Size in bytes of the library's own device scratch used by paged_attention_forward_noalloc (32 MiB per

@@ -45,7 +45,9 @@ attn_kernel(const AttnParams p) {
   // writes these words (only the queue counter beside them changes, through vector atomics).  Read per item
   // instead, they would be vector loads, and each item would wait a memory round trip before its copies.
   const CONST_AS int* const hdr = (const CONST_AS int*)p.buf.hdr;
-  const int total_items = hdr[kHdrUnits] * Hkv;
+  // A plan made for another call shape is not run (split_reduce_kernel then fills the output with NaN).
+  const bool plan_ok = hdr[kHdrSig0] == p.sig[0] && hdr[kHdrSig1] == p.sig[1] && hdr[kHdrSig2] == p.sig[2];
+  const int total_items = plan_ok ? hdr[kHdrUnits] * Hkv : 0;
   const PlanWords pw{hdr[kHdrPartition], hdr[kHdrPartitionWide], hdr[kHdrPrefKeys], hdr[kHdrPrefTable],
                      hdr[kHdrPrefPartition]};
   // The next item is claimed while the current one finishes (after its last stage), so the atomic's

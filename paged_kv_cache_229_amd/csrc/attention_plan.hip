@@ -240,6 +240,9 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       p.buf.hdr[kHdrTiles] = 0;
       p.buf.hdr[kHdrBadSeqs] = -1;
       p.buf.hdr[kHdrPrefN] = 0;
+      p.buf.hdr[kHdrSig0] = p.sig[0];
+      p.buf.hdr[kHdrSig1] = p.sig[1];
+      p.buf.hdr[kHdrSig2] = p.sig[2];
     }
     return;
   }
@@ -367,7 +370,14 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       }
       int sum;
       const int first = run + block_exclusive_scan<kPlanWaves>(pr, &sum, red);
-      if (tau < total_tiles) p.buf.tile_rec[tau] = make_int4(rec.x, rec.y, np > 1 ? first : -1, np);
+      if (tau < total_tiles) {
+        p.buf.tile_rec[tau] = make_int4(rec.x, rec.y, np > 1 ? first : -1, np);
+        // The sequence's query range as planned, for split_reduce_kernel (which then never reads the call's
+        // query_start_loc, so a later call on this plan stays inside the planned partial rows).
+        int n, L;
+        seq(rec.x, n, L);
+        p.buf.tile_q[tau] = make_int2(rec.x < kSeqCache ? seqc[rec.x].w : qsl[rec.x], n);
+      }
       run += sum;
     }
   }
@@ -456,35 +466,43 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     p.buf.hdr[kHdrPrefTable] = pb;
     p.buf.hdr[kHdrPrefPartition] = Pv;
     p.buf.hdr[kHdrPrefParts] = npv;
+    p.buf.hdr[kHdrSig0] = p.sig[0];
+    p.buf.hdr[kHdrSig1] = p.sig[1];
+    p.buf.hdr[kHdrSig2] = p.sig[2];
   }
+}
 
-  // Rejected sequences (q_len > context, negative context, context past the table) get NaN output rows,
-  // so that bad metadata shows in the result without a host check.  A sequence whose query range itself
-  // is inconsistent owns no rows and is left alone.  Each wave takes its own sequences; a wave-wide loop
-  // fills the rows of each rejected one.  Rare: skipped unless the first pass found a rejected sequence.
-  if (total_bad > 0 && p.out != nullptr) {
-    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};  // eight bf16 NaNs
-    const int lane = tid & 63;
-    for (int base = tid - lane; base < N; base += kPlanThreads) {
-      const int s = base + lane;
-      int lo = 0, hi = 0;
-      bool poison = false;
-      if (s < N) {
-        lo = qsl[s];
-        hi = qsl[s + 1];
-        poison = lo >= 0 && hi > lo && hi <= p.total_q && !seq_ok(lo, hi, ctx[s], p.total_q, p.max_context);
-      }
-      unsigned long long m = __builtin_amdgcn_ballot_w64(poison);
-      while (m) {
-        const int b = __builtin_ctzll(m);
-        m &= m - 1;
-        const int blo = __builtin_amdgcn_readlane(lo, b);
-        const int bhi = __builtin_amdgcn_readlane(hi, b);
-        u32x4v* const o = static_cast<u32x4v*>(p.out) + static_cast<int64_t>(blo) * p.out_row_chunks;
-        const int64_t chunks = static_cast<int64_t>(bhi - blo) * p.out_row_chunks;
-        for (int64_t c = lane; c < chunks; c += 64) o[c] = nan8;
-      }
+// bf16 NaN rows for the sequences a plan rejected (q_len > context, negative context, context past the table):
+// bad metadata shows in the result without a host check.  A sequence whose query range itself is inconsistent
+// owns no rows and is left alone.  Called by every thread of one workgroup (THREADS threads, whole waves); each
+// wave takes its own sequences and a wave-wide loop fills the rows of each rejected one.
+template <int THREADS, int D>
+__device__ void fill_rejected_rows(const AttnParams& p) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};  // eight bf16 NaNs
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int N = p.num_seqs;
+  const int max_context = p.max_blocks_per_seq << p.block_size_log2;
+  const int row_chunks = p.num_q_heads * D * 2 / 16;
+  for (int base = tid - lane; base < N; base += THREADS) {
+    const int s = base + lane;
+    int lo = 0, hi = 0;
+    bool poison = false;
+    if (s < N) {
+      lo = p.query_start_loc[s];
+      hi = p.query_start_loc[s + 1];
+      poison = lo >= 0 && hi > lo && hi <= p.total_q && !seq_ok(lo, hi, p.context_lens[s], p.total_q, max_context);
+    }
+    unsigned long long m = __builtin_amdgcn_ballot_w64(poison);
+    while (m) {
+      const int b = __builtin_ctzll(m);
+      m &= m - 1;
+      const int blo = __builtin_amdgcn_readlane(lo, b);
+      const int bhi = __builtin_amdgcn_readlane(hi, b);
+      u32x4v* const o = static_cast<u32x4v*>(p.out) + static_cast<int64_t>(blo) * row_chunks;
+      const int64_t chunks = static_cast<int64_t>(bhi - blo) * row_chunks;
+      for (int64_t c = lane; c < chunks; c += 64) o[c] = nan8;
     }
   }
 }
@@ -499,13 +517,30 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
   constexpr int RPW = kThreads / D4;  // rows per workgroup
   const int tile_idx = blockIdx.x;
   const int g = blockIdx.y;
+  const int block = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  // The attention kernel has finished (stream order): reset its item queue, so that a later call may run on
+  // this plan again.
+  if (block == 0 && threadIdx.x == 0) p.buf.hdr[kHdrQueue] = 0;
+  if (p.buf.hdr[kHdrSig0] != p.sig[0] || p.buf.hdr[kHdrSig1] != p.sig[1] || p.buf.hdr[kHdrSig2] != p.sig[2]) {
+    // The workspace holds no plan for this call's shape (the attention kernel did nothing): the whole output
+    // becomes NaN, grid-strided.
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    const int64_t chunks = p.total_q * p.num_q_heads * D * 2 / 16;
+    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * gridDim.y * gridDim.z * kThreads;
+    for (int64_t c = static_cast<int64_t>(block) * kThreads + threadIdx.x; c < chunks; c += nthreads)
+      static_cast<u32x4v*>(p.out)[c] = nan8;
+    return;
+  }
+  if (block == 0 && p.buf.hdr[kHdrBadSeqs] > 0) fill_rejected_rows<kThreads, D>(p);
   if (tile_idx >= p.buf.hdr[kHdrTiles]) return;
   const int4 rec = p.buf.tile_rec[tile_idx];
   const int np = rec.w;
   if (np <= 1) return;
-  const int s = rec.x, tile = rec.y, pb0 = rec.z;
-  const int q0 = p.query_start_loc[s];
-  const int n = p.query_start_loc[s + 1] - q0;
+  const int tile = rec.y, pb0 = rec.z;
+  const int2 tq = p.buf.tile_q[tile_idx];
+  const int q0 = tq.x;
+  const int n = tq.y;
   const int G = p.group;
   const int RT = tile_rows_of(tile_kind_for(n * G, p.tile_kind));
   const int row0 = tile * RT;

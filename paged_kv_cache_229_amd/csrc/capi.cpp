@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 thread_local std::string g_error;
 thread_local int g_partition_keys = 0;
@@ -83,7 +83,7 @@ int check_pool(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_
 }
 
 struct WsLayout {
-  size_t hdr, seq_tiles, tile_rec, units, part_ml, part_acc, tok_info, total;
+  size_t hdr, seq_tiles, tile_rec, tile_q, units, part_ml, part_acc, tok_info, total;
   int64_t tile_cap, unit_cap, prow_cap;
 };
 
@@ -108,6 +108,8 @@ WsLayout workspace_layout(int32_t num_seqs, int64_t total_q, int32_t num_q_heads
   off = round256(off + static_cast<size_t>(num_seqs) * sizeof(int));
   w.tile_rec = off;
   off = round256(off + static_cast<size_t>(w.tile_cap) * 4 * sizeof(int));
+  w.tile_q = off;
+  off = round256(off + static_cast<size_t>(w.tile_cap) * 2 * sizeof(int));
   w.units = off;
   off = round256(off + static_cast<size_t>(w.unit_cap) * 8 * sizeof(int));
   const size_t part_rows = static_cast<size_t>(partial_rows);
@@ -256,15 +258,16 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int64_t total_q, int32_t
 
 namespace {
 
-// Both attention entry points.  `prefix` enables the shared-prefix pass (and the 256-row tiles it runs
-// on); its range was checked by the caller.
+// Every attention entry point.  `prefix` enables the shared-prefix pass (and the 256-row tiles it runs
+// on); its range was checked by the caller.  run_only: the workspace already holds this call's plan (left by
+// an earlier call with the same metadata): no planning launch.
 int attention_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                    const int32_t* query_start_loc, int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                    int64_t block_stride, float scale, int32_t dtype, int32_t max_q_len_hint,
                    const pkv::PrefixParams* prefix, void* workspace, size_t workspace_bytes, void* stream,
-                   bool noalloc = false) {
+                   bool noalloc = false, bool run_only = false) {
   if (num_seqs < 0 || total_q < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs and total_q must be >= 0");
   int64_t stride = 0;
   const int rc = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
@@ -350,12 +353,32 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   b.hdr = reinterpret_cast<int*>(ws + w.hdr);
   b.seq_tiles = reinterpret_cast<int*>(ws + w.seq_tiles);
   b.tile_rec = reinterpret_cast<int4*>(ws + w.tile_rec);
+  b.tile_q = reinterpret_cast<int2*>(ws + w.tile_q);
   b.units = reinterpret_cast<int4*>(ws + w.units);
   b.part_ml = reinterpret_cast<float2*>(ws + w.part_ml);
   b.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
   b.tok_info = reinterpret_cast<int4*>(ws + w.tok_info);
   p.buf = b;
   p.tile_kind = tile_kind;
+  // Signature of this call's shape (plan header words kHdrSig0..2): everything the plan's records and the
+  // workspace layout depend on besides the metadata's contents.  A run on an existing plan checks it on the
+  // device (FNV-1a over the shape words).
+  uint32_t h = 2166136261u;
+  for (const int64_t v : {static_cast<int64_t>(num_q_heads), static_cast<int64_t>(num_kv_heads),
+                          static_cast<int64_t>(head_dim), static_cast<int64_t>(block_size),
+                          static_cast<int64_t>(max_blocks_per_seq), static_cast<int64_t>(tile_kind),
+                          static_cast<int64_t>(narrow_only), w.tile_cap, w.unit_cap, w.prow_cap,
+                          static_cast<int64_t>(prefix ? prefix->begin : -1),
+                          static_cast<int64_t>(prefix ? prefix->end : -1),
+                          static_cast<int64_t>(prefix ? prefix->tokens : -1)}) {
+    for (int byte = 0; byte < 8; ++byte) {
+      h ^= static_cast<uint32_t>((v >> (8 * byte)) & 0xff);
+      h *= 16777619u;
+    }
+  }
+  p.sig[0] = num_seqs;
+  p.sig[1] = static_cast<int>(total_q);
+  p.sig[2] = static_cast<int>(h);
 
   pkv::PlanParams pp{};
   pp.context_lens = context_lens;
@@ -377,11 +400,13 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   pp.prow_cap = static_cast<int>(w.prow_cap);
   if (prefix) pp.prefix = *prefix;
   pp.buf = b;
-  pp.out = out;
-  pp.out_row_chunks = num_q_heads * head_dim * 2 / 16;
+  for (int i = 0; i < 3; ++i) pp.sig[i] = p.sig[i];
 
-  hipError_t e = pkv::launch_plan(pp, st);
-  if (e != hipSuccess) return hip_fail("plan launch", e);
+  hipError_t e = hipSuccess;
+  if (!run_only) {
+    e = pkv::launch_plan(pp, st);
+    if (e != hipSuccess) return hip_fail("plan launch", e);
+  }
   int64_t grid = grid_wgs;
   const int64_t max_items = w.unit_cap * num_kv_heads;
   if (grid > max_items) grid = max_items;
@@ -410,6 +435,18 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                         query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
                         num_blocks, block_stride, scale, dtype, max_q_len_hint, nullptr, workspace,
                         workspace_bytes, stream);
+}
+
+int paged_attention_run(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        const int32_t* query_start_loc, int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                        int64_t block_stride, float scale, int32_t dtype, int32_t max_q_len_hint, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, block_stride, scale, dtype, max_q_len_hint, nullptr, workspace,
+                        workspace_bytes, stream, /*noalloc=*/false, /*run_only=*/true);
 }
 
 int paged_attention_forward_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -61,6 +61,10 @@ enum HeaderWord {
   kHdrPrefTable = 10,
   kHdrPrefPartition = 11,
   kHdrPrefParts = 12,
+  // The call shape the plan was made for (PlanParams::sig): a call that runs on an existing plan checks it.
+  kHdrSig0 = 13,
+  kHdrSig1 = 14,
+  kHdrSig2 = 15,
 };
 // Tiles with more rows than this (long query chunks) are split only over long contexts: their partial
 // rows cost as much to write and merge as a good share of the keys they would save reading, and there are
@@ -74,6 +78,7 @@ struct PlanBuffers {
   int* hdr;         // [16]
   int* seq_tiles;   // [num_seqs]  scratch
   int4* tile_rec;   // [tile_cap]  {sequence, tile, first partial row or -1, number of partitions}
+  int2* tile_q;     // [tile_cap]  the tile's sequence's {first query token, query tokens}, as planned
   // [unit_cap][2]: {sequence, tile, first key of the partition, first partial row or -1 if unsplit}, then the
   // sequence's {first query token, query tokens, context length} and the tile kind (1 or 2), so that an item
   // needs no further dependent metadata load
@@ -117,11 +122,7 @@ struct PlanParams {
   int prow_cap;
   PrefixParams prefix;
   PlanBuffers buf;
-  // Output rows of sequences the plan rejects (q_len > context, negative context, context past the table)
-  // are filled with NaN when their query range is consistent: out is [total_q][out_row_chunks] 16-byte
-  // chunks of bf16.
-  void* out;
-  int out_row_chunks;
+  int sig[3];  // call-shape signature, written to the header words kHdrSig0..2
 };
 
 struct AttnParams {
@@ -145,6 +146,10 @@ struct AttnParams {
   float scale;           // natural-exponent scale
   float scale_log2;      // scale * log2(e)
   PlanBuffers buf;
+  // Signature of the call shape (PlanParams::sig).  The kernels run the plan in the workspace only if its
+  // header carries the same words; otherwise the attention kernel does nothing and split_reduce_kernel fills
+  // the whole output with NaN.
+  int sig[3];
 };
 
 // Words of the plan header every work item needs, read once per workgroup (scalar loads) before the first
