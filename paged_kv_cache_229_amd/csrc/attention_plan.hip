@@ -144,7 +144,11 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   constexpr int kPlanThreads = THREADS;
   constexpr int kPlanWaves = THREADS / 64;
   constexpr int kBucketsPerThread = kSortBuckets / THREADS;
-  __shared__ int bucket[kSortBuckets];
+  // Sorting scratch: kSortBuckets counters for longest-first order; to interleave the two tile classes, also
+  // per-class stage counts (twice: one copy hands out the ranks of the key histogram, the other those of the
+  // scatter) and work offsets.
+  __shared__ int sortbuf[7 * kSortBuckets];
+  int* const bucket = sortbuf;
   __shared__ int4 seqc[kSeqCache];  // (n, L, tiles, first query token) per sequence
   const int tid = threadIdx.x;
   __shared__ int red[kPlanWaves];
@@ -334,19 +338,21 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   };
 
   // Lengthen P until the units and the split tiles' partial rows fit the workspace.
-  int units_total = 0;
+  int units_total = 0, units_wide = 0;  // units in all, and units of 256-row tiles (the prefix sequence's included)
   for (;;) {
     const int Pw = wide_len(P);
     const FastDiv divp(P), divw(Pw);
-    int units = 0, prows = 0;
+    int units = 0, prows = 0, wide = 0;
     for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
       int len, k0, np_own, rows_t, km;
       int wt;
       const int np = tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
       units = min(units + np_own, kSat);
+      if (wt == 2) wide = min(wide + np_own, kSat);
       if (np > 1) prows = min(prows + min(np * rows_t, kSat) * Hkv, kSat);
     }
     units_total = block_sum<kPlanWaves>(units, red) + units_v;
+    units_wide = block_sum<kPlanWaves>(wide, red) + units_v;
     const int prows_total = block_sum<kPlanWaves>(prows, red);
     if ((units_total <= p.unit_cap && prows_total <= p.prow_cap) || P >= max_kmax) break;
     P = P > pmax / 2 ? pmax : 2 * P;
@@ -382,21 +388,108 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     }
   }
 
-  // Counting sort of the units by stage count, longest first: histogram, bucket offsets, scatter.
+  // Order of the units.  Longest first on the stage count weighted by kind_weight (a counting sort), unless the
+  // call has both tile classes with at least one item per workgroup of the grid each: units of 128-row tiles
+  // (the 16-row body, paced by the K/V copies) and of 256-row tiles (the 32-row body, bound by the matrix
+  // cores) are then interleaved -- each unit's key is the fraction of its class's work (longest first within
+  // the class) that precedes it, quantised to kSortBuckets steps, and the units are counting-sorted on it --
+  // so that throughout the call some workgroups compute long query chunks while others stream K/V, instead of
+  // every workgroup computing chunks first (HBM idle) and streaming last (HBM saturated, each workgroup
+  // slower).  Each class still ends on its shortest units.  A class with few items (the shared-prefix pass's
+  // equally long prefix units) is not spread out: an even spread would start some of them last.
+  const long long grid_wgs = p.min_items > 0 ? p.min_items / 2 : 256;
+  const bool interleave = static_cast<long long>(units_total - units_wide) * Hkv >= grid_wgs &&
+                          static_cast<long long>(units_wide) * Hkv >= grid_wgs;
+  int* const cnt = sortbuf + kSortBuckets;       // [2][kSortBuckets] units per class and stage bucket
+  int* const cumw = sortbuf + 3 * kSortBuckets;  // [2][kSortBuckets] class work before each stage bucket
+  int* const cnt2 = sortbuf + 5 * kSortBuckets;  // [2][kSortBuckets] copy of cnt
+  // Exact integer keys (the histogram and the scatter compute them separately and must agree bit for bit):
+  // key = floor(x * kSortBuckets / W) for class work x <= W, with x and W shifted right alike so that the
+  // product stays below 2^31, and the division by the class's W through FastDiv.
+  int wshift0 = 0, wshift1 = 0;
+  FastDiv wdiv0(2), wdiv1(2);
+  // Merge key of the unit of class c, stage bucket b, rank r within the bucket.
+  auto merge_key = [&](int c, int b, int r) -> int {
+    const int stages = kSortBuckets - 1 - b;
+    const long long x = cumw[c * kSortBuckets + b] + static_cast<long long>(r) * stages * kind_weight(c + 1);
+    const int xs = static_cast<int>(x >> (c == 0 ? wshift0 : wshift1)) * kSortBuckets;
+    return min(kSortBuckets - 1, (c == 0 ? wdiv0 : wdiv1).floor_div(xs));
+  };
+  if (interleave) {
+    for (int i = tid; i < 3 * kSortBuckets; i += kPlanThreads) sortbuf[i] = 0;  // key counters and cnt[][]
+    __syncthreads();
+    for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
+      int len, k0, np_own, rows_t, km;
+      int wt;
+      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
+      for (int k = k0; k < km; k += len) atomicAdd(&cnt[(wt == 2) * kSortBuckets + sort_bucket(min(km - k, len), 1)], 1);
+    }
+    for (int i = tid; i < units_v; i += kPlanThreads) {
+      const int k = (i % npv) * Pv;
+      atomicAdd(&cnt[kSortBuckets + sort_bucket(min(ptok - k, Pv), 1)], 1);
+    }
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kBucketsPerThread; ++i) bucket[tid * kBucketsPerThread + i] = 0;
-  __syncthreads();
-  for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
-    int len, k0, np_own, rows_t, km;
-    int wt;
-    tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
-    for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len), wt)], 1);
+    for (int c = 0; c < 2; ++c) {
+      int mine = 0;
+#pragma unroll
+      for (int i = 0; i < kBucketsPerThread; ++i) {
+        const int b = tid * kBucketsPerThread + i;
+        mine += cnt[c * kSortBuckets + b] * (kSortBuckets - 1 - b) * kind_weight(c + 1);
+      }
+      int total;
+      int off = block_exclusive_scan<kPlanWaves>(mine, &total, red);
+#pragma unroll
+      for (int i = 0; i < kBucketsPerThread; ++i) {
+        const int b = tid * kBucketsPerThread + i;
+        cumw[c * kSortBuckets + b] = off;
+        cnt2[c * kSortBuckets + b] = cnt[c * kSortBuckets + b];
+        off += cnt[c * kSortBuckets + b] * (kSortBuckets - 1 - b) * kind_weight(c + 1);
+      }
+      const int sh = max(0, 32 - __builtin_clz(static_cast<unsigned>(max(total, 1))) - 21);
+      const FastDiv dv(max(total >> sh, 2));
+      if (c == 0) {
+        wshift0 = sh;
+        wdiv0 = dv;
+      } else {
+        wshift1 = sh;
+        wdiv1 = dv;
+      }
+    }
+    __syncthreads();
+    // Merge-key histogram (bucket[] counts keys): the scatter's walk over the units, with ranks handed out by
+    // cnt2, so that every (class, stage bucket, rank) is counted once, as the scatter will place it.
+    for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
+      int len, k0, np_own, rows_t, km;
+      int wt;
+      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
+      for (int k = k0; k < km; k += len) {
+        const int c = wt == 2, b = sort_bucket(min(km - k, len), 1);
+        atomicAdd(&bucket[merge_key(c, b, atomicSub(&cnt2[c * kSortBuckets + b], 1) - 1)], 1);
+      }
+    }
+    for (int i = tid; i < units_v; i += kPlanThreads) {
+      const int b = sort_bucket(min(ptok - (i % npv) * Pv, Pv), 1);
+      atomicAdd(&bucket[merge_key(1, b, atomicSub(&cnt2[kSortBuckets + b], 1) - 1)], 1);
+    }
+    __syncthreads();
+  } else {
+    // Counting sort of the units by weighted stage count, longest first: histogram, bucket offsets, scatter.
+#pragma unroll
+    for (int i = 0; i < kBucketsPerThread; ++i) bucket[tid * kBucketsPerThread + i] = 0;
+    __syncthreads();
+    for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
+      int len, k0, np_own, rows_t, km;
+      int wt;
+      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
+      for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len), wt)], 1);
+    }
+    for (int i = tid; i < units_v; i += kPlanThreads) {
+      const int k = (i % npv) * Pv;
+      atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv), kind_weight(2))], 1);
+    }
+    __syncthreads();
   }
-  for (int i = tid; i < units_v; i += kPlanThreads) {
-    const int k = (i % npv) * Pv;
-    atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv), kind_weight(2))], 1);
-  }
-  __syncthreads();
   {
     int c[kBucketsPerThread];
     int mine = 0;
@@ -414,6 +507,13 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     }
   }
   __syncthreads();
+  // Slot of the next unit of class c (1: 256-row tiles) in stage bucket b (unweighted stage count).
+  auto place = [&](int c, int b) -> int {
+    if (!interleave)  // the weighted stage count's bucket, as in the histogram
+      return atomicAdd(&bucket[kSortBuckets - 1 - min((kSortBuckets - 1 - b) * kind_weight(c + 1), kSortBuckets - 1)], 1);
+    const int r = atomicSub(&cnt[c * kSortBuckets + b], 1) - 1;  // ranks count down: no clearing
+    return atomicAdd(&bucket[merge_key(c, b, r)], 1);
+  };
 
   for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
     const int4 rec = p.buf.tile_rec[tau];
@@ -432,7 +532,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     }
     for (int pp = 0; pp < np_own; ++pp) {
       const int kb = k0 + pp * len;
-      const int slot = atomicAdd(&bucket[sort_bucket(min(km - kb, len), wt)], 1);
+      const int slot = place(wt == 2, sort_bucket(min(km - kb, len), 1));
       p.buf.units[2 * slot] = make_int4(rec.x, rec.y, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
       p.buf.units[2 * slot + 1] = sq;
     }
@@ -448,7 +548,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   for (int i = tid; i < units_v; i += kPlanThreads) {
     const int tv = i / npv;
     const int k = (i - tv * npv) * Pv;
-    const int slot = atomicAdd(&bucket[sort_bucket(min(ptok - k, Pv), kind_weight(2))], 1);
+    const int slot = place(1, sort_bucket(min(ptok - k, Pv), 1));
     p.buf.units[2 * slot] = make_int4(N, tv, k, -1);
     p.buf.units[2 * slot + 1] = make_int4(vq0, vn, ptok - 1 + vn, 2);
   }
