@@ -50,15 +50,11 @@ attn_kernel(const AttnParams p) {
   const int total_items = plan_ok ? hdr[kHdrUnits] * Hkv : 0;
   const PlanWords pw{hdr[kHdrPartition], hdr[kHdrPartitionWide], hdr[kHdrPrefKeys], hdr[kHdrPrefTable],
                      hdr[kHdrPrefPartition]};
-  // The next item is claimed while the current one finishes (after its last stage), so the atomic's
-  // latency hides behind the epilogue.
+  // Workgroup w starts on item w without a claim (the first claims of all workgroups at once would queue on
+  // one counter); each later item is claimed while the current one finishes (after its last stage), so the
+  // atomic's latency hides behind the epilogue, and the queue hands out gridDim.x, gridDim.x + 1, ...
   int next_item = 0;
-  if (tid == 0) next_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
-  for (;;) {
-    if (tid == 0) s_item = next_item;
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
-    __syncthreads();
+  for (int item = blockIdx.x;;) {
     if (item >= total_items) break;
     const int unit = item / Hkv;
     const int g = item - unit * Hkv;
@@ -70,6 +66,10 @@ attn_kernel(const AttnParams p) {
       if (kind == 2) wide_item<D, kWideHalves>(p, pw, smem, unit, g, next_item);
       else narrow_item<D>(p, pw, smem, unit, g, next_item);
     }
+    if (tid == 0) s_item = next_item;
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
   }
 }
 

@@ -342,7 +342,8 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
       if (st + 4 < nst) fetch_table(st + 4, tbn);
     }
 
-    if (tid == 0) next_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
+    // (workgroup w's first item was item w: the queue hands out the items from gridDim.x on)
+    if (tid == 0) next_item = static_cast<int>(gridDim.x) + atomicAdd(p.buf.hdr + kHdrQueue, 1);
 
     float lsum[NTW];
 #pragma unroll

@@ -362,7 +362,8 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
       if (st + 4 < nst) fetch_table(st + 4, tbn);
     }
 
-    if (tid == 0) next_item = atomicAdd(p.buf.hdr + kHdrQueue, 1);
+    // (workgroup w's first item was item w: the queue hands out the items from gridDim.x on)
+    if (tid == 0) next_item = static_cast<int>(gridDim.x) + atomicAdd(p.buf.hdr + kHdrQueue, 1);
     float lrow[NH];  // the rows' sums over both halves of the keys
 #pragma unroll
     for (int h = 0; h < NH; ++h) lrow[h] = pair_sum(lw[h]);
