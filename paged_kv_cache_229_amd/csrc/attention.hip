@@ -48,8 +48,7 @@ attn_kernel(const AttnParams p) {
   // A plan made for another call shape is not run (split_reduce_kernel then fills the output with NaN).
   const bool plan_ok = hdr[kHdrSig0] == p.sig[0] && hdr[kHdrSig1] == p.sig[1] && hdr[kHdrSig2] == p.sig[2];
   const int total_items = plan_ok ? hdr[kHdrUnits] * Hkv : 0;
-  const PlanWords pw{hdr[kHdrPartition], hdr[kHdrPartitionWide], hdr[kHdrPrefKeys], hdr[kHdrPrefTable],
-                     hdr[kHdrPrefPartition]};
+  const PlanWords pw{hdr[kHdrPrefKeys], hdr[kHdrPrefTable], hdr[kHdrPrefPartition]};
   // Workgroup w starts on item w without a claim (the first claims of all workgroups at once would queue on
   // one counter); each later item is claimed while the current one finishes (after its last stage), so the
   // atomic's latency hides behind the epilogue, and the queue hands out gridDim.x, gridDim.x + 1, ...
@@ -61,8 +60,8 @@ attn_kernel(const AttnParams p) {
     if (NARROW_ONLY) {
       narrow_item<D>(p, pw, smem, unit, g, next_item);
     } else {
-      // The unit's row-tile kind (word 7 of its record), through a scalar load.
-      const int kind = ((const CONST_AS int*)p.buf.units)[8 * unit + 7];
+      // The unit's row-tile kind (low bits of word 7 of its record), through a scalar load.
+      const int kind = ((const CONST_AS int*)p.buf.units)[8 * unit + 7] & 3;
       if (kind == 2) wide_item<D, kWideHalves>(p, pw, smem, unit, g, next_item);
       else narrow_item<D>(p, pw, smem, unit, g, next_item);
     }

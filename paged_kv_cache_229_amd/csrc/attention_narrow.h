@@ -85,8 +85,6 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
   const int Hq = p.num_q_heads;
-  const int P = pw.P;
-  const int Pw = pw.Pw;
   const int bs_log2 = p.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int last_block = static_cast<int>(p.num_blocks - 1);
@@ -130,7 +128,7 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;
-    const int ke = min(kmax, kb + (rows_here > kSmallTileRows ? Pw : P));
+    const int ke = min(kmax, kb + (urec[7] >> 2));  // the partition's key count, from the plan
     const int WR = rows_here <= T::WROWS ? 1
                    : rows_here <= 2 * T::WROWS ? 2
                    : rows_here <= 4 * T::WROWS ? 4 : 8;

@@ -60,6 +60,22 @@ struct TileGeom {
   }
 };
 
+// A tile's own partitions (keys [k0, km)): nb partitions of len keys over [k0, kbulk), then late pieces of at
+// most `piece` keys over [kbulk, km); n in all.  len, piece and kbulk - k0 are multiples of kStageKeys, so every
+// partition starts on a stage boundary counted from k0.
+struct OwnParts {
+  int k0, km, len, nb, kbulk, piece, n;
+  __device__ void range(int pp, int& kb, int& kl) const {
+    if (pp < nb) {
+      kb = k0 + pp * len;
+      kl = min(len, kbulk - kb);
+    } else {
+      kb = kbulk + (pp - nb) * piece;
+      kl = min(piece, km - kb);
+    }
+  }
+};
+
 // Stage-count bucket of a unit, longest first.  A stage of a 256-row tile (32-row waves, bound by the matrix
 // cores) takes about twice as long as a stage of a 128-row tile (16-row waves, bound by the copies), so the
 // former count double (weight 2): units are ordered by estimated time, not key count.
@@ -317,11 +333,14 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   }
   const int units_v = tiles_v * npv;
 
-  // Partitions of tile record rec for partition lengths (P_, Pw_).  Its own key range starts at *k0
-  // (after the prefix for members of the shared-prefix pass) and has *np_own partitions of *len keys;
-  // returns all partitions of the tile including the prefix ones.  Also gives the tile's rows and kmax.
-  auto tile_parts = [&](const int4 rec, int P_, int Pw_, const FastDiv& dp, const FastDiv& dw, int& len, int& k0,
-                        int& np_own, int& rows_t, int& km, int& wt) -> int {
+  // Partitions of tile record rec for partition lengths (P_, Pw_).  Its own key range starts at k0 (after the
+  // prefix for members of the shared-prefix pass); returns all partitions of the tile including the prefix
+  // ones.  Also gives the tile's rows and kind weight.  Late pieces (kLateMinPartition): a split small tile
+  // of a call with long partitions ends on pieces of max(P_ / 4, kLatePieceMin) keys covering the last
+  // kLateNum / kLateDen of its keys, so that the queue ends on short items.
+  const bool late_on = p.forced_partition <= 0 && !pref;
+  auto tile_parts = [&](const int4 rec, int P_, int Pw_, const FastDiv& dp, const FastDiv& dw, OwnParts& op,
+                        int& rows_t, int& wt) -> int {
     int n, L;
     const int s = rec.x, t = rec.y;
     seq(s, n, L);
@@ -329,12 +348,24 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const TileGeom geo = geom(rows);
     wt = kind_weight(geo.kind);
     rows_t = min(geo.RT, rows - t * geo.RT);
-    km = geo.kmax(L, n, rows, t);
+    op.km = geo.kmax(L, n, rows, t);
     const bool member = pref && s >= pb && s < pe;
-    k0 = member ? ptok : 0;
-    len = rows_t > kSmallTileRows ? Pw_ : P_;
-    np_own = rows_t > kSmallTileRows ? dw.ceil_div(km - k0) : dp.ceil_div(km - k0);
-    return np_own + (member ? npv : 0);
+    op.k0 = member ? ptok : 0;
+    const bool small = rows_t <= kSmallTileRows;
+    op.len = small ? P_ : Pw_;
+    const int keys = op.km - op.k0;
+    op.kbulk = op.km;
+    op.piece = op.len;
+    if (late_on && small && P_ >= kLateMinPartition && keys > P_) {
+      op.piece = max(P_ / 4 / kStageKeys * kStageKeys, kLatePieceMin);
+      // Every partition starts a whole number of stages after k0: the copies resolve one block-table entry per
+      // group of keys, which must not straddle a block.
+      const int late = static_cast<int>(static_cast<long long>(keys) * kLateNum / kLateDen);
+      op.kbulk = op.k0 + (keys - late) / kStageKeys * kStageKeys;
+    }
+    op.nb = small ? dp.ceil_div(op.kbulk - op.k0) : dw.ceil_div(op.kbulk - op.k0);
+    op.n = op.nb + (op.km - op.kbulk + op.piece - 1) / op.piece;
+    return op.n + (member ? npv : 0);
   };
 
   // Lengthen P until the units and the split tiles' partial rows fit the workspace.
@@ -344,11 +375,11 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const FastDiv divp(P), divw(Pw);
     int units = 0, prows = 0, wide = 0;
     for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
-      int len, k0, np_own, rows_t, km;
-      int wt;
-      const int np = tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
-      units = min(units + np_own, kSat);
-      if (wt == 2) wide = min(wide + np_own, kSat);
+      OwnParts op;
+      int rows_t, wt;
+      const int np = tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, op, rows_t, wt);
+      units = min(units + op.n, kSat);
+      if (wt == 2) wide = min(wide + op.n, kSat);
       if (np > 1) prows = min(prows + min(np * rows_t, kSat) * Hkv, kSat);
     }
     units_total = block_sum<kPlanWaves>(units, red) + units_v;
@@ -369,9 +400,9 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       int4 rec = make_int4(0, 0, -1, 0);
       if (tau < total_tiles) {
         rec = p.buf.tile_rec[tau];
-        int len, k0, np_own, rows_t, km;
-        int wt;
-        np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
+        OwnParts op;
+        int rows_t, wt;
+        np = tile_parts(rec, P, Pw, divp, divw, op, rows_t, wt);
         if (np > 1) pr = np * rows_t * Hkv;
       }
       int sum;
@@ -419,10 +450,14 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     for (int i = tid; i < 3 * kSortBuckets; i += kPlanThreads) sortbuf[i] = 0;  // key counters and cnt[][]
     __syncthreads();
     for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
-      int len, k0, np_own, rows_t, km;
-      int wt;
-      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
-      for (int k = k0; k < km; k += len) atomicAdd(&cnt[(wt == 2) * kSortBuckets + sort_bucket(min(km - k, len), 1)], 1);
+      OwnParts op;
+      int rows_t, wt;
+      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, op, rows_t, wt);
+      for (int pp = 0; pp < op.n; ++pp) {
+        int kb, kl;
+        op.range(pp, kb, kl);
+        atomicAdd(&cnt[(wt == 2) * kSortBuckets + sort_bucket(kl, 1)], 1);
+      }
     }
     for (int i = tid; i < units_v; i += kPlanThreads) {
       const int k = (i % npv) * Pv;
@@ -460,11 +495,13 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     // Merge-key histogram (bucket[] counts keys): the scatter's walk over the units, with ranks handed out by
     // cnt2, so that every (class, stage bucket, rank) is counted once, as the scatter will place it.
     for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
-      int len, k0, np_own, rows_t, km;
-      int wt;
-      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
-      for (int k = k0; k < km; k += len) {
-        const int c = wt == 2, b = sort_bucket(min(km - k, len), 1);
+      OwnParts op;
+      int rows_t, wt;
+      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, op, rows_t, wt);
+      for (int pp = 0; pp < op.n; ++pp) {
+        int kb, kl;
+        op.range(pp, kb, kl);
+        const int c = wt == 2, b = sort_bucket(kl, 1);
         atomicAdd(&bucket[merge_key(c, b, atomicSub(&cnt2[c * kSortBuckets + b], 1) - 1)], 1);
       }
     }
@@ -479,10 +516,14 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     for (int i = 0; i < kBucketsPerThread; ++i) bucket[tid * kBucketsPerThread + i] = 0;
     __syncthreads();
     for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
-      int len, k0, np_own, rows_t, km;
-      int wt;
-      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
-      for (int k = k0; k < km; k += len) atomicAdd(&bucket[sort_bucket(min(km - k, len), wt)], 1);
+      OwnParts op;
+      int rows_t, wt;
+      tile_parts(p.buf.tile_rec[tau], P, Pw, divp, divw, op, rows_t, wt);
+      for (int pp = 0; pp < op.n; ++pp) {
+        int kb, kl;
+        op.range(pp, kb, kl);
+        atomicAdd(&bucket[sort_bucket(kl, wt)], 1);
+      }
     }
     for (int i = tid; i < units_v; i += kPlanThreads) {
       const int k = (i % npv) * Pv;
@@ -517,9 +558,9 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
 
   for (int tau = tid; tau < total_tiles; tau += kPlanThreads) {
     const int4 rec = p.buf.tile_rec[tau];
-    int len, k0, np_own, rows_t, km;
-    int wt;
-    const int np = tile_parts(rec, P, Pw, divp, divw, len, k0, np_own, rows_t, km, wt);
+    OwnParts op;
+    int rows_t, wt;
+    const int np = tile_parts(rec, P, Pw, divp, divw, op, rows_t, wt);
     const int pr = rec.z;
     int4 sq;  // the sequence's first query token, query tokens and context, and its tile kind
     if (rec.x < kSeqCache) {
@@ -530,18 +571,19 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
       const int n = qsl[rec.x + 1] - lo;
       sq = make_int4(lo, n, ctx[rec.x], tile_kind_for(n * G, p.tile_kind));
     }
-    for (int pp = 0; pp < np_own; ++pp) {
-      const int kb = k0 + pp * len;
-      const int slot = place(wt == 2, sort_bucket(min(km - kb, len), 1));
+    for (int pp = 0; pp < op.n; ++pp) {
+      int kb, kl;
+      op.range(pp, kb, kl);
+      const int slot = place(wt == 2, sort_bucket(kl, 1));
       p.buf.units[2 * slot] = make_int4(rec.x, rec.y, kb, np > 1 ? pr + pp * rows_t * Hkv : -1);
-      p.buf.units[2 * slot + 1] = sq;
+      p.buf.units[2 * slot + 1] = make_int4(sq.x, sq.y, sq.z, sq.w | (kl << 2));
     }
-    if (np > np_own) {
+    if (np > op.n) {
       // member of the shared-prefix pass (one tile): its query tokens find their prefix partial rows here
       const int s = rec.x;
       const int q_lo = qsl[s];
       const int n = rows_t / G;
-      const int4 info = make_int4(s, pr + np_own * rows_t * Hkv, rows_t, q_lo);
+      const int4 info = make_int4(s, pr + op.n * rows_t * Hkv, rows_t, q_lo);
       for (int i = 0; i < n; ++i) p.buf.tok_info[q_lo - vq0 + i] = info;
     }
   }
@@ -550,7 +592,7 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
     const int k = (i - tv * npv) * Pv;
     const int slot = place(1, sort_bucket(min(ptok - k, Pv), 1));
     p.buf.units[2 * slot] = make_int4(N, tv, k, -1);
-    p.buf.units[2 * slot + 1] = make_int4(vq0, vn, ptok - 1 + vn, 2);
+    p.buf.units[2 * slot + 1] = make_int4(vq0, vn, ptok - 1 + vn, 2 | (min(Pv, ptok - k) << 2));
   }
   if (tid == 0) {
     p.buf.hdr[kHdrUnits] = units_total;

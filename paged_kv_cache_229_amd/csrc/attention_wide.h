@@ -94,8 +94,6 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
   const int Hq = p.num_q_heads;
-  const int P = pw.P;
-  const int Pw = pw.Pw;
   // Shared-prefix sequence (index num_seqs in the unit records; absent when it has no tokens).
   const int pre_keys = pw.pre_keys;
   const int pre_table = pw.pre_table;
@@ -151,7 +149,7 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
     const int row0 = tile * T::RT;
     const int rows_here = min(T::RT, n * G - row0);
     const int kmax = L - n + (row0 + rows_here - 1) / G + 1;
-    const int ke = pre ? min(min(kmax, kb + pre_P), pre_keys) : min(kmax, kb + (rows_here > kSmallTileRows ? Pw : P));
+    const int ke = pre ? min(min(kmax, kb + pre_P), pre_keys) : min(kmax, kb + (urec[7] >> 2));
     const int pre_part = pre ? kb / pre_P : 0;  // partition of the prefix sequence
     // Waves split the rows (WAVE_ROWS each) when there are enough, else the keys: WR row groups x WK key
     // groups.

@@ -47,7 +47,7 @@ constexpr int kNoSplitSlackDen = 10;
 enum HeaderWord {
   kHdrUnits = 0,
   kHdrQueue = 1,
-  kHdrPartition = 2,      // partition length of tiles with at most kSmallTileRows rows
+  kHdrPartition = 2,      // partition length of tiles with at most kSmallTileRows rows (before late pieces)
   kHdrTiles = 3,
   kHdrBadSeqs = 4,
   kHdrPartitionWide = 5,  // partition length of taller tiles
@@ -71,6 +71,15 @@ enum HeaderWord {
 // already many of them.  Their partition is at least kWidePartitionMin keys.
 constexpr int kSmallTileRows = 64;
 constexpr int kWidePartitionMin = 4096;
+// Late pieces.  In a call whose small tiles are split into long partitions (P >= kLateMinPartition keys), each
+// split small tile's last kLateNum / kLateDen of keys become pieces of max(P / 4, kLatePieceMin) keys.  Sorted
+// longest first, they are the queue's last items, so that the workgroups' last items are short and they
+// finish closer together; with shorter partitions (short contexts) the extra items' fills cost more than the
+// tail saves.
+constexpr int kLateMinPartition = 4096;
+constexpr int kLateNum = 3;
+constexpr int kLateDen = 20;
+constexpr int kLatePieceMin = 1024;
 
 // Device work plan, all in the caller's workspace.  A unit is (sequence, row tile, context partition);
 // every unit is processed once per kv head.
@@ -80,8 +89,8 @@ struct PlanBuffers {
   int4* tile_rec;   // [tile_cap]  {sequence, tile, first partial row or -1, number of partitions}
   int2* tile_q;     // [tile_cap]  the tile's sequence's {first query token, query tokens}, as planned
   // [unit_cap][2]: {sequence, tile, first key of the partition, first partial row or -1 if unsplit}, then the
-  // sequence's {first query token, query tokens, context length} and the tile kind (1 or 2), so that an item
-  // needs no further dependent metadata load
+  // sequence's {first query token, query tokens, context length} and the tile kind (1 or 2) | the partition's
+  // key count << 2, so that an item needs no further dependent metadata load
   int4* units;
   float2* part_ml;  // [prow_cap]  running max (log2 units) and sum per partial row
   float* part_acc;  // [prow_cap * head_dim] unnormalised partial outputs
@@ -153,9 +162,9 @@ struct AttnParams {
 };
 
 // Words of the plan header every work item needs, read once per workgroup (scalar loads) before the first
-// item: partition lengths, and the shared-prefix sequence's key count, table row and partition length.
+// item: the shared-prefix sequence's key count, table row and partition length.
 struct PlanWords {
-  int P, Pw, pre_keys, pre_table, pre_P;
+  int pre_keys, pre_table, pre_P;
 };
 
 struct KvWriteParams {

@@ -323,6 +323,36 @@ def test_single_long_decode_keeps_the_grid_busy():
     check_close(out_f64(out), outs[0], BF16, "single long decode")
 
 
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_late_pieces(block_size):
+    """Long partitions (a small item target gives P of about 4900 keys) over contexts that end off any stage
+    boundary: each split tile's last keys become late pieces (more units than whole partitions of P give),
+    which must start on stage boundaries like every other partition; checked against the oracle with
+    multi-token queries."""
+    ctx = [9001, 12345, 17003, 10477, 15555, 13131]
+    w = build_workload(np.random.default_rng(47 + block_size), name="late", dtype=BF16, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=block_size, q_lens=[1, 4, 8, 3, 1, 6],
+                       context_lens=ctx)
+    log(f"late pieces, block size {block_size}")
+    pkv.set_tuning(0, 32, 0)
+    dw = DeviceWorkload(w)
+    st = dw.steps[0]
+    ws = torch.zeros(max(256, pkv.workspace_size(w.num_seqs, st["q"].shape[0], w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, st["q"].dtype, st["max_q_len"])),
+                     dtype=torch.uint8, device=st["q"].device)
+    pkv.paged_kv_write(st["k_new"], st["v_new"], st["slot_mapping"], dw.k_pool, dw.v_pool)
+    out = pkv.paged_attention_forward(st["q"], dw.k_pool, dw.v_pool, dw.block_tables, st["context_lens"],
+                                      st["query_start_loc"], scale=w.scale, workspace=ws,
+                                      max_q_len=st["max_q_len"])
+    torch.cuda.synchronize()
+    hdr = ws[:64].cpu().numpy().view(np.int32)
+    units, partition = int(hdr[0]), int(hdr[2])
+    whole = sum(-(-int(c) // partition) for c in st["context_lens"].cpu().numpy())
+    assert partition >= 4096 and units > whole, (partition, units, whole)
+    _, _, outs = _oracle_steps(w)
+    check_close(out_f64(out), outs[0], BF16, f"late pieces, block size {block_size}")
+
+
 def test_empty_and_degenerate():
     """num_seqs == 0 and num_tokens == 0 are no-ops; q_len 0 sequences are skipped."""
     w = build_workload(np.random.default_rng(5), name="deg", dtype=BF16, num_q_heads=8, num_kv_heads=2,
