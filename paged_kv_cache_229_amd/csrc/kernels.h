@@ -32,7 +32,11 @@ __host__ __device__ inline int tile_kind_for(int rows, int forced) {
 }
 // Upper bound on the automatic work-item target (items = units x kv heads).
 constexpr int kMaxItems = 4096;
-constexpr int kDefaultItems = 768;
+// Automatic target: 576 items (about 2.25 per workgroup of the persistent grid).  With late pieces ending
+// the queue, longer bulk partitions are cheaper: the speculative batch (32 sequences over 8K-32K keys) takes
+// 439-441 us at 512-576 against 449-451 us at 768; decode, the mixed step and the shared-prefix batch are
+// unchanged within noise (decode's partitions are set by kSoftMinPartition).
+constexpr int kDefaultItems = 576;
 constexpr int kMinPartition = 256;
 // With the automatic item target, partitions are lengthened up to this many keys as long as the call
 // keeps PlanParams::min_items items: every item costs a pipeline fill and an epilogue, so fewer, longer
