@@ -323,7 +323,7 @@ int pkv_cm_build_tables(const pkv_cache_manager* manager, const int64_t* seq_ids
  *   target_items    > 0: aim the automatic choice at this many (tile, kv head, partition) work items;
  *                   0 = default (about 576 items, with partitions of at least 2048 keys as long as the
  *                   call keeps two items per workgroup of the attention grid; a call with partitions of
- *                   4096 keys or more ends each split tile on shorter late pieces).
+ *                   2048 keys or more ends each split tile on shorter late pieces).
  *   tile_kind       0 = automatic: 1 when max_q_len_hint * (num_q_heads / num_kv_heads) <= 128,
  *                   else 2; 1 = 128-row tiles (16 rows per wave); 2 = 256-row tiles (32 rows per wave).
  */
