@@ -124,8 +124,9 @@ def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, pr
     on the stream.  The same number of steps then runs again with events on the launch stream, for the
     attention kernel alone (HIP events the library records around it) and the whole attention call (plan +
     attention + split reduce: torch events around the call).  reuse: the pool copies stand for the layers
-    of a model step, which share the metadata: the call on copy 0 plans (paged_attention_forward), the calls
-    on the other copies run on its plan (paged_attention_run)."""
+    of a model step, which share the metadata: the call on copy 0 plans (paged_attention_forward, or
+    paged_attention_forward_prefix with prefix_pass), the calls on the other copies run on its plan
+    (paged_attention_run, paged_attention_run_prefix)."""
     import numpy as np
     import torch
 
@@ -165,7 +166,10 @@ def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, pr
         pkv.paged_kv_write(kn, vn, sm, kp, vp)
         if timed is not None:
             call_ev[timed][0].record()
-        if prefix_tokens:
+        if prefix_tokens and reuse and i % len(pools) != 0:
+            pkv.paged_attention_run_prefix(q, kp, vp, bt, cl, qsl, 0, w.num_seqs, prefix_tokens,
+                                           scale=w.scale, out=out, workspace=ws)
+        elif prefix_tokens:
             pkv.paged_attention_forward_prefix(q, kp, vp, bt, cl, qsl, 0, w.num_seqs, prefix_tokens,
                                                scale=w.scale, out=out, workspace=ws)
         elif reuse and i % len(pools) != 0:
@@ -364,7 +368,7 @@ def main() -> None:
                     help="time only the sequences with q_len > 1 (prefill) or q_len == 1 (decode)")
     ap.add_argument("--plan-reuse", action="store_true",
                     help="the pool copies are the layers of one model step: plan on the first, run the others "
-                         "on that plan (paged_attention_run)")
+                         "on that plan (paged_attention_run, or paged_attention_run_prefix with --prefix-pass)")
     ap.add_argument("--prefix-pass", action="store_true",
                     help="prefix workload: attend the shared blocks once for all sequences "
                          "(paged_attention_forward_prefix)")
@@ -410,10 +414,6 @@ def main() -> None:
         w.description += f" [{args.subset} sequences only: {len(keep)}]"
     print(f"[bench] generated {w.description} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
-    if args.plan_reuse and args.prefix_pass:
-        print("bench.py: --plan-reuse runs plain calls on a reused plan; it does not combine with --prefix-pass",
-              file=sys.stderr)
-        sys.exit(2)
     if args.prefix_pass and w.shared_prefix_blocks == 0:
         print("bench.py: --prefix-pass needs a workload with shared prefix blocks (prefix)", file=sys.stderr)
         sys.exit(2)

@@ -239,6 +239,29 @@ int paged_attention_forward_prefix(void* out, const void* q, const void* k_cache
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_run_prefix — paged_attention_forward_prefix on the work plan an earlier
+ * paged_attention_forward_prefix call left in `workspace`, without planning again: for the layers after the
+ * first of a model step whose batch shares a prefix (the same sharing in every layer, since every layer's
+ * pool uses the same block tables; ADR 004 "Paged Attention Serving Integration", Decision 4).  Call
+ * paged_attention_forward_prefix for the step's first layer and this for the others, with the same
+ * workspace, metadata (contents included), sizes, prefix_begin / prefix_end / prefix_tokens and tuning; out,
+ * q, k_cache, v_cache and scale may differ.  The result is then identical to paged_attention_forward_prefix's
+ * with the same arguments.
+ *  - Same arguments and errors as paged_attention_forward_prefix.
+ *  - If the workspace holds no plan for this shape and prefix range (none, or one that paged_attention_forward
+ *    or another range made), nothing is computed and every output element is NaN; otherwise as
+ *    paged_attention_run.
+ * PKV_FP32 has no plan and runs as paged_attention_forward.
+ */
+int paged_attention_run_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                               int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, int64_t block_stride, float scale,
+                               int32_t dtype, int32_t prefix_begin, int32_t prefix_end, int32_t prefix_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_kv_copy_blocks — for i < num_pairs: block dst_blocks[i] of both caches takes the contents of
  * block src_blocks[i] (this layer's block_size * num_kv_heads * head_dim elements, bit for bit).  The
  * device half of copy on write: run it with the (src, dst) pair pkv_cm_append reports, before writing the

@@ -45,6 +45,7 @@ __all__ = [
     "paged_attention_forward_prefix",
     "paged_attention_forward_noalloc",
     "paged_attention_run",
+    "paged_attention_run_prefix",
     "workspace_size",
     "prefix_workspace_size",
     "set_tuning",
@@ -275,6 +276,32 @@ def paged_attention_forward_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cac
         block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q,
         hq, hkv, d, bs, nb, stride, scale, _dtype_code(q), int(prefix_begin), int(prefix_end),
         int(prefix_tokens), workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return out
+
+
+def paged_attention_run_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               block_tables: torch.Tensor, context_lens: torch.Tensor,
+                               query_start_loc: torch.Tensor, prefix_begin: int, prefix_end: int,
+                               prefix_tokens: int, scale: float | None = None, out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``paged_attention_forward_prefix`` on the work plan the last call with this ``workspace`` made (the
+    binding's own workspace for this device and stream when none is given), without planning again: for the
+    layers after the first of a model step; see ``paged_attention_run_prefix`` in include/paged_kv.h.  A
+    workspace holding no plan for this call's shape and prefix range gives an all-NaN output."""
+    dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, scale = _attention_args(
+        q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, False)
+    need = prefix_workspace_size(num_seqs, total_q, hq, hkv, d, q.dtype)
+    if workspace is None:
+        workspace = _WORKSPACES.get((dev.index, torch.cuda.current_stream(dev).cuda_stream))
+        if need > 0 and (workspace is None or workspace.numel() < need):
+            raise ValueError("no plan to run: call paged_attention_forward_prefix with this metadata first")
+    workspace = _workspace(workspace, need, dev) if workspace is not None else None
+    check(lib().paged_attention_run_prefix(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q,
+        hq, hkv, d, bs, nb, stride, scale, _dtype_code(q), int(prefix_begin), int(prefix_end), int(prefix_tokens),
+        workspace.data_ptr() if workspace is not None else None, workspace.numel() if workspace is not None else 0,
+        _stream(dev)))
     return out
 
 

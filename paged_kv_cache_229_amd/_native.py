@@ -53,6 +53,9 @@ SIGNATURES = {
     "paged_attention_forward_prefix": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
                                                   _i32, _i32, _i32, _i32, _i64, _i64, _f32, _i32, _i32,
                                                   _i32, _i32, _vp, _sz, _vp]),
+    "paged_attention_run_prefix": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
+                                              _i32, _i32, _i32, _i32, _i64, _i64, _f32, _i32, _i32,
+                                              _i32, _i32, _vp, _sz, _vp]),
     "paged_attention_set_tuning": (_c.c_int, [_i32, _i32, _i32]),
     "paged_attention_set_profile_events": (_c.c_int, [_vp, _vp]),
     "paged_kv_copy_blocks": (_c.c_int, [_vp, _vp, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),

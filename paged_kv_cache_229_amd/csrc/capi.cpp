@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 thread_local std::string g_error;
 thread_local int g_partition_keys = 0;
@@ -493,6 +493,26 @@ int paged_attention_forward_prefix(void* out, const void* q, const void* k_cache
   return attention_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                         query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
                         num_blocks, block_stride, scale, dtype, 0, &pre, workspace, workspace_bytes, stream);
+}
+
+int paged_attention_run_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                               int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, int64_t block_stride, float scale,
+                               int32_t dtype, int32_t prefix_begin, int32_t prefix_end, int32_t prefix_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (prefix_begin < 0 || prefix_end < prefix_begin || prefix_end > num_seqs || prefix_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "need 0 <= prefix_begin <= prefix_end <= num_seqs and prefix_tokens >= 0");
+  if (block_size > 0 && prefix_tokens % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG, "prefix_tokens must be a multiple of block_size");
+  if (static_cast<int64_t>(prefix_tokens) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "prefix_tokens exceeds max_blocks_per_seq * block_size");
+  const pkv::PrefixParams pre{prefix_begin, prefix_end, prefix_tokens};
+  return attention_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, block_stride, scale, dtype, 0, &pre, workspace, workspace_bytes, stream,
+                        /*noalloc=*/false, /*run_only=*/true);
 }
 
 int paged_attention_set_tuning(int32_t partition_keys, int32_t target_items, int32_t tile_kind) {

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
         assert name in N.SIGNATURES, f"{name} declared in the header but not bound"
         assert hasattr(lib, name), f"{name} not exported"
     assert set(N.SIGNATURES) == set(names)
-    assert lib.paged_kv_abi_version() == 5
+    assert lib.paged_kv_abi_version() == 6
 
 
 def test_single_hip_runtime_loaded():

@@ -1,6 +1,6 @@
-"""paged_attention_run: the layers of a model step after the first run on the work plan the first layer's
-paged_attention_forward left in the workspace (same metadata, each layer its own pools, queries and new K/V).
-Every layer's output is bit-identical to paged_attention_forward's on that layer and within tolerance of the
+"""paged_attention_run (and paged_attention_run_prefix): the layers of a model step after the first run on
+the work plan the first layer's paged_attention_forward (_prefix) left in the workspace (same metadata, each
+layer its own pools, queries and new K/V).  Every layer's output is bit-identical to paged_attention_forward's on that layer and within tolerance of the
 oracle; a workspace without a plan for the call's shape gives an all-NaN output; rejected sequences still
 get NaN rows on a run; the float32 path (no plan) runs as paged_attention_forward."""
 
@@ -39,9 +39,10 @@ def _device_step(w, st):
                 max_q_len=int(np.max(np.diff(st.query_start_loc), initial=0)))
 
 
-def _run_layers(w, ctx=None):
+def _run_layers(w, ctx=None, prefix_tokens=0):
     """Forward on layer 0, run on layers 1..LAYERS-1, and a fresh forward on every layer (own workspace) for
-    comparison.  Returns [(run or layer-0 output, fresh forward output, layer pools and step)]."""
+    comparison; with prefix_tokens, the shared-prefix entry points over all sequences.  Returns [(run or
+    layer-0 output, fresh forward output, layer pools and step)]."""
     st = w.steps[0]
     if ctx is not None:
         st = dataclasses.replace(st, context_lens=ctx)
@@ -49,6 +50,9 @@ def _run_layers(w, ctx=None):
     s0 = _device_step(w, st)
     need = pkv.workspace_size(w.num_seqs, s0["q"].shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim,
                               s0["q"].dtype, s0["max_q_len"])
+    if prefix_tokens:
+        need = pkv.prefix_workspace_size(w.num_seqs, s0["q"].shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                         s0["q"].dtype)
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=s0["q"].device)
     ws_fresh = torch.zeros_like(ws)
     res = []
@@ -58,9 +62,15 @@ def _run_layers(w, ctx=None):
         kp, vp = to_torch(kp_h, w.dtype), to_torch(vp_h, w.dtype)
         pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], kp, vp)
         args = (s["q"], kp, vp, bt, s["context_lens"], s["query_start_loc"])
-        call = pkv.paged_attention_forward if l == 0 else pkv.paged_attention_run
-        out = call(*args, scale=w.scale, workspace=ws, max_q_len=s["max_q_len"])
-        fresh = pkv.paged_attention_forward(*args, scale=w.scale, workspace=ws_fresh, max_q_len=s["max_q_len"])
+        if prefix_tokens:
+            pre = (0, w.num_seqs, prefix_tokens)
+            call = pkv.paged_attention_forward_prefix if l == 0 else pkv.paged_attention_run_prefix
+            out = call(*args, *pre, scale=w.scale, workspace=ws)
+            fresh = pkv.paged_attention_forward_prefix(*args, *pre, scale=w.scale, workspace=ws_fresh)
+        else:
+            call = pkv.paged_attention_forward if l == 0 else pkv.paged_attention_run
+            out = call(*args, scale=w.scale, workspace=ws, max_q_len=s["max_q_len"])
+            fresh = pkv.paged_attention_forward(*args, scale=w.scale, workspace=ws_fresh, max_q_len=s["max_q_len"])
         res.append((out, fresh, kp_h, vp_h, st_l))
     torch.cuda.synchronize()
     return res
@@ -76,6 +86,21 @@ def test_layers_reuse_the_first_plan(name):
         if l == LAYERS - 1:
             _, _, ref = oracle.run_step(kp_h, vp_h, w.block_tables, st_l, w.scale, w.dtype)
             check_close(got, ref, w.dtype, f"{name} layer {l} (run) vs oracle")
+
+
+def test_layers_reuse_the_shared_prefix_plan():
+    """paged_attention_run_prefix on the plan paged_attention_forward_prefix made for the first layer: every
+    layer bit-identical to a fresh paged_attention_forward_prefix and, on the last, to the oracle."""
+    w = make_config("prefix", "small")
+    prefix_tokens = w.shared_prefix_blocks * w.block_size
+    assert prefix_tokens > 0
+    log(f"shared-prefix plan reuse over {LAYERS} layers: small prefix, {prefix_tokens} shared tokens")
+    for l, (out, fresh, kp_h, vp_h, st_l) in enumerate(_run_layers(w, prefix_tokens=prefix_tokens)):
+        got = out_f64(out)
+        assert np.array_equal(got, out_f64(fresh)), f"prefix layer {l}: run differs from a fresh forward"
+        if l == LAYERS - 1:
+            _, _, ref = oracle.run_step(kp_h, vp_h, w.block_tables, st_l, w.scale, w.dtype)
+            check_close(got, ref, w.dtype, f"prefix layer {l} (run_prefix) vs oracle")
 
 
 def test_forced_partitions_and_tile_kinds():
@@ -98,7 +123,8 @@ def _small(seed, q_lens, ctx, dtype=BF16, hq=8, hkv=2, d=128):
 
 def test_no_plan_for_the_shape_gives_nan():
     """A run on a zeroed workspace, on a plan for another batch shape, and on a plan the shared-prefix entry
-    point made: every output element NaN, nothing else written."""
+    point made, and a shared-prefix run on a zeroed workspace, a plain forward's plan and another prefix
+    range's plan: every output element NaN, nothing else written."""
     w = _small(61, [1, 3, 2], [40, 70, 33])
     w2 = _small(62, [1, 1, 2, 1], [40, 70, 33, 90])
     s, s2 = _device_step(w, w.steps[0]), _device_step(w2, w2.steps[0])
@@ -119,6 +145,17 @@ def test_no_plan_for_the_shape_gives_nan():
         log(f"run without a plan for its shape: {what}")
         out = torch.zeros_like(s["q"])
         pkv.paged_attention_run(*args, scale=w.scale, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(out.float()).all().item(), what
+    for what in ("zeroed workspace", "plan of a plain forward", "plan for another prefix range"):
+        ws = torch.zeros(need, dtype=torch.uint8, device=s["q"].device)
+        if what == "plan of a plain forward":
+            pkv.paged_attention_forward(*args, scale=w.scale, workspace=ws)
+        elif what == "plan for another prefix range":
+            pkv.paged_attention_forward_prefix(*args, 0, w.num_seqs - 1, 16, scale=w.scale, workspace=ws)
+        log(f"shared-prefix run without a plan for its range: {what}")
+        out = torch.zeros_like(s["q"])
+        pkv.paged_attention_run_prefix(*args, 0, w.num_seqs, 16, scale=w.scale, out=out, workspace=ws)
         torch.cuda.synchronize()
         assert torch.isnan(out.float()).all().item(), what
 
