@@ -117,7 +117,8 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int64_t total_q, int32_t
  *   out           (device) [total_q][num_q_heads][head_dim], written
  *   q             (device) [total_q][num_q_heads][head_dim], contiguous
  *   k_cache, v_cache (device) one layer's pool (layout above), read only
- *   block_tables  (device) [num_seqs][max_blocks_per_seq] int32, row-major
+ *   block_tables  (device) [num_seqs][max_blocks_per_seq] int32, row-major; max_blocks_per_seq >= 1 and
+ *                 max_blocks_per_seq * block_size < 2^29 (else PKV_ERR_INVALID_ARG / PKV_ERR_UNSUPPORTED)
  *   context_lens  (device) [num_seqs] int32
  *   query_start_loc (device) [num_seqs + 1] int32, query_start_loc[0] == 0, query_start_loc[num_seqs]
  *                 == total_q; a sequence with n == 0 is skipped

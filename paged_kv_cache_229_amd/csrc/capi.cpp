@@ -275,8 +275,9 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
   if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
-  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size must be < 2^31");
+  // The plan packs a partition's key count into the upper 30 bits of a 32-bit word.
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 29))
+    return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size must be < 2^29");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
   const int group = num_q_heads / num_kv_heads;
   if (total_q * group > INT32_MAX / 2 || total_q * num_q_heads > INT32_MAX)

@@ -95,6 +95,7 @@ def _fwd(**over):
     (dict(dtype=3), N.PKV_ERR_UNSUPPORTED),
     (dict(mbps=0), N.PKV_ERR_INVALID_ARG),
     (dict(mbps=1 << 28), N.PKV_ERR_UNSUPPORTED),
+    (dict(mbps=1 << 25), N.PKV_ERR_UNSUPPORTED),   # 2^29 keys at block size 16: the plan's 30-bit key counts
     (dict(scale=float("inf")), N.PKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), N.PKV_ERR_INVALID_ARG),
     (dict(scale=0.0), N.PKV_ERR_INVALID_ARG),
