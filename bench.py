@@ -118,7 +118,7 @@ def _to_device(dev, a, is_data=True):
 
 
 def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, prefix_pass: bool = False,
-               graph: bool = False, reuse: bool = False) -> dict:
+               graph: bool = False, reuse: bool = False, fused: bool = False) -> dict:
     """Warm up, then time exactly ``steps`` steps (paged_kv_write + paged_attention_forward of the workload's
     step, each on the next of ``copies`` pool copies) between two device synchronisations, with nothing else
     on the stream.  The same number of steps then runs again with events on the launch stream, for the
@@ -126,7 +126,8 @@ def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, pr
     attention + split reduce: torch events around the call).  reuse: the pool copies stand for the layers
     of a model step, which share the metadata: the call on copy 0 plans (paged_attention_forward, or
     paged_attention_forward_prefix with prefix_pass), the calls on the other copies run on its plan
-    (paged_attention_run, paged_attention_run_prefix)."""
+    (paged_attention_run, paged_attention_run_prefix).  fused: each step is one paged_attention_write_forward
+    call (the write and the plan share a launch); the call events then also cover the write."""
     import numpy as np
     import torch
 
@@ -163,6 +164,14 @@ def time_steps(dev, w, steps: int, warmup: int, copies: int, layers: int = 1, pr
 
     def step(i, timed=None):
         kp, vp = pools[i % len(pools)]
+        if fused:
+            if timed is not None:
+                call_ev[timed][0].record()
+            pkv.paged_attention_write_forward(kn, vn, sm, q, kp, vp, bt, cl, qsl, scale=w.scale, out=out,
+                                              workspace=ws, max_q_len=max_q)
+            if timed is not None:
+                call_ev[timed][1].record()
+            return
         pkv.paged_kv_write(kn, vn, sm, kp, vp)
         if timed is not None:
             call_ev[timed][0].record()
@@ -280,6 +289,19 @@ def plan_reuse_view(dev, name: str, steps: int, warmup: int, copies: int) -> dic
             "attention_call_frac": round(cgbs / HBM_PEAK_GBS, 4)}
 
 
+def fused_step_view(dev, name: str, steps: int, warmup: int, copies: int) -> dict:
+    """The workload's step through paged_attention_write_forward: the K/V write and the work plan share one
+    launch, so a step is three launches instead of four.  Wall time per step, beside the plain step's."""
+    from workloads import make_config
+
+    w = make_config(name, "full")
+    work = algorithmic_work(w)
+    t = time_steps(dev, w, steps, warmup, copies, fused=True)
+    sgbs = (work["attn_bytes_unique"] + work["write_bytes"]) / (t["ms_per_step"] * 1e-3) / 1e9
+    return {"workload": w.name, "ms_per_step": round(t["ms_per_step"], 4),
+            "step_frac": round(sgbs / HBM_PEAK_GBS, 4), "write_and_call_ms": t["call"]}
+
+
 def prefill_view(dev, steps: int, warmup: int, copies: int) -> dict:
     """The other half of the metric: the chunked-prefill step's 8 prefill chunks alone (512 tokens each over a
     prior context U[0, 2048], the launch `--workload mixed --subset prefill` times), with the attention kernel
@@ -369,6 +391,8 @@ def main() -> None:
     ap.add_argument("--plan-reuse", action="store_true",
                     help="the pool copies are the layers of one model step: plan on the first, run the others "
                          "on that plan (paged_attention_run, or paged_attention_run_prefix with --prefix-pass)")
+    ap.add_argument("--fused", action="store_true",
+                    help="each step is one paged_attention_write_forward call (write and plan in one launch)")
     ap.add_argument("--prefix-pass", action="store_true",
                     help="prefix workload: attend the shared blocks once for all sequences "
                          "(paged_attention_forward_prefix)")
@@ -417,6 +441,10 @@ def main() -> None:
     if args.prefix_pass and w.shared_prefix_blocks == 0:
         print("bench.py: --prefix-pass needs a workload with shared prefix blocks (prefix)", file=sys.stderr)
         sys.exit(2)
+    if args.fused and (args.prefix_pass or args.plan_reuse or args.graph):
+        print("bench.py: --fused times plain steps through paged_attention_write_forward; it does not combine "
+              "with --prefix-pass, --plan-reuse or --graph", file=sys.stderr)
+        sys.exit(2)
     work = algorithmic_work(w)
     traffic_key = w.name if args.subset == "all" else f"{w.name}:{args.subset}"
     if args.prefix_pass:
@@ -424,7 +452,7 @@ def main() -> None:
     kernel_name = kernel_name_for(w, args.tile_kind, args.prefix_pass)
     pkv.set_tuning(args.partition, args.items, args.tile_kind)  # the workspace size depends on it
     t = time_steps(dev, w, args.steps, args.warmup, args.copies, layers=args.layers,
-                   prefix_pass=args.prefix_pass, graph=args.graph, reuse=args.plan_reuse)
+                   prefix_pass=args.prefix_pass, graph=args.graph, reuse=args.plan_reuse, fused=args.fused)
     print(f"[bench] headline timed: {t['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
 
     ms_step = t["ms_per_step"]
@@ -453,6 +481,7 @@ def main() -> None:
                    "pool_copies": t["pool_copies"],
                    "pool_layout": "per_layer" if args.layers == 1 else f"layer_in_block x{args.layers}",
                    "shared_prefix_pass": bool(args.prefix_pass), "plan_reuse": bool(args.plan_reuse),
+                   "fused_write": bool(args.fused),
                    "launch": t["launch"]},
         "tokens_per_s": round(work["total_q"] / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -478,7 +507,7 @@ def main() -> None:
     if work["prefill_flops"]:
         result["prefill_subset_flops"] = work["prefill_flops"]
     default_shape = (args.workload == "spec" and args.subset == "all" and args.layers == 1 and not args.graph
-                     and not args.prefix_pass and not args.plan_reuse
+                     and not args.prefix_pass and not args.plan_reuse and not args.fused
                      and not (args.partition or args.items or args.tile_kind))
     if default_shape and not args.no_views:
         torch.cuda.empty_cache()
@@ -491,6 +520,9 @@ def main() -> None:
         result["plan_reuse_view"] = [plan_reuse_view(dev, name, args.steps, args.warmup, args.copies)
                                      for name in ("spec", "decode")]
         print("[bench] plan-reuse views timed", file=sys.stderr, flush=True)
+        result["fused_step_view"] = [fused_step_view(dev, name, args.steps, args.warmup, args.copies)
+                                     for name in ("spec", "decode")]
+        print("[bench] fused-step views timed", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, work, args.cpu_budget)
     print(json.dumps(result), flush=True)

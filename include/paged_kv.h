@@ -142,6 +142,29 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                             void* stream);
 
 /*
+ * paged_attention_write_forward — paged_kv_write(k_new, v_new, slot_mapping, num_tokens into k_cache,
+ * v_cache) followed by paged_attention_forward(...) on the same pool: the same results (pools and output
+ * bit-identical to the two calls), one launch fewer.  A decode step writes the step's new K/V rows and then
+ * attends over them (flash-attention issue 660, the prefill/decode discussion; "Paged Attention 基础 –
+ * 原理与实现进度", §3.2 status table: slot mapping); the work planner reads only the metadata, so it runs in
+ * the same launch as the write (workgroup 0 plans, the others write) instead of after it.
+ *   k_new, v_new, slot_mapping, num_tokens  as paged_kv_write's k, v, slot_mapping, num_tokens (num_tokens
+ *                 == 0 writes nothing); the pool arguments (k_cache, v_cache, num_blocks, block_size,
+ *                 block_stride, num_kv_heads, head_dim, dtype) serve both.
+ *   everything else as paged_attention_forward.
+ * Errors: those of paged_kv_write, then those of paged_attention_forward; on any error nothing is launched.
+ * PKV_FP32 (no plan) and a call with no query rows write with a launch of their own.
+ */
+int paged_attention_write_forward(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                  int64_t num_tokens, void* out, const void* q, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                                  int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks, int64_t block_stride, float scale,
+                                  int32_t dtype, int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * paged_attention_run — paged_attention_forward on the work plan an earlier call left in `workspace`,
  * without planning again.  Every layer of a model step calls attention with its own k_cache[i], v_cache[i]
  * but the same block tables and lengths (ADR 004 "Paged Attention Serving Integration", Decision 4), and

@@ -42,6 +42,7 @@ from ._native import (  # noqa: F401
 __all__ = [
     "paged_kv_write",
     "paged_attention_forward",
+    "paged_attention_write_forward",
     "paged_attention_forward_prefix",
     "paged_attention_forward_noalloc",
     "paged_attention_run",
@@ -95,11 +96,7 @@ def _int32_vec(t: torch.Tensor, name: str):
         raise TypeError(f"{name} must be a contiguous int32 tensor")
 
 
-def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
-                   v_cache: torch.Tensor, *, validate: bool = False) -> None:
-    """Store row t of ``k``/``v`` ``[T, H_kv, D]`` at pool row ``slot_mapping[t]`` (block =
-    slot // block_size, offset = slot % block_size) of ``k_cache``/``v_cache``; negative slots are
-    skipped.  Asynchronous on the current stream."""
+def _write_args(k, v, slot_mapping, k_cache, v_cache, validate):
     dev = _same_device(k, v, slot_mapping, k_cache, v_cache)
     nb, bs, hkv, d, stride = _pool_geometry(k_cache, v_cache)
     if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (hkv, d):
@@ -113,6 +110,15 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
         raise ValueError("slot_mapping must have one entry per token")
     if validate:
         validate_metadata(slot_mapping=slot_mapping, num_blocks=nb, block_size=bs)
+    return dev, nb, bs, hkv, d, stride
+
+
+def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, *, validate: bool = False) -> None:
+    """Store row t of ``k``/``v`` ``[T, H_kv, D]`` at pool row ``slot_mapping[t]`` (block =
+    slot // block_size, offset = slot % block_size) of ``k_cache``/``v_cache``; negative slots are
+    skipped.  Asynchronous on the current stream."""
+    dev, nb, bs, hkv, d, stride = _write_args(k, v, slot_mapping, k_cache, v_cache, validate)
     check(lib().paged_kv_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k.shape[0],
                                k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, stride, hkv, d,
                                _dtype_code(k), _stream(dev)))
@@ -207,6 +213,28 @@ def paged_attention_forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q,
         hq, hkv, d, bs, nb, stride, scale, _dtype_code(q), hint, workspace.data_ptr(),
         workspace.numel(), _stream(dev)))
+    return out
+
+
+def paged_attention_write_forward(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                                  q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  query_start_loc: torch.Tensor, scale: float | None = None,
+                                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                  max_q_len: int | None = None, validate: bool = False) -> torch.Tensor:
+    """``paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache)`` then ``paged_attention_forward(q,
+    k_cache, v_cache, ...)``: the same pools and output, one launch fewer (the work plan is made in the
+    write's launch); see ``paged_attention_write_forward`` in include/paged_kv.h."""
+    _write_args(k_new, v_new, slot_mapping, k_cache, v_cache, validate)
+    dev, nb, bs, hkv, d, stride, total_q, hq, num_seqs, out, scale = _attention_args(
+        q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, validate)
+    hint = -1 if max_q_len is None else int(max_q_len)
+    workspace = _workspace(workspace, workspace_size(num_seqs, total_q, hq, hkv, d, q.dtype, max_q_len), dev)
+    check(lib().paged_attention_write_forward(
+        k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_new.shape[0], out.data_ptr(),
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), query_start_loc.data_ptr(), num_seqs, total_q, hq, hkv, d, bs, nb, stride,
+        scale, _dtype_code(q), hint, workspace.data_ptr(), workspace.numel(), _stream(dev)))
     return out
 
 

@@ -45,6 +45,9 @@ SIGNATURES = {
     "paged_attention_forward": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
                                            _i32, _i32, _i32, _i64, _i64, _f32, _i32, _i32, _vp, _sz,
                                            _vp]),
+    "paged_attention_write_forward": (_c.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                                 _i32, _i64, _i32, _i32, _i32, _i32, _i64, _i64, _f32, _i32,
+                                                 _i32, _vp, _sz, _vp]),
     "paged_attention_run": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
                                        _i32, _i32, _i32, _i64, _i64, _f32, _i32, _i32, _vp, _sz, _vp]),
     "paged_attention_forward_noalloc": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,

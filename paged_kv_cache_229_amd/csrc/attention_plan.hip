@@ -27,6 +27,7 @@
 // merging the partial softmax sums gives the same result up to float32 rounding order.
 #include "fastdiv.h"
 #include "kernels.h"
+#include "kv_write_body.h"
 
 namespace pkv {
 namespace {
@@ -155,8 +156,9 @@ __device__ inline int block_exclusive_scan(int v, int* total, int* red) {
   return before + incl - v;
 }
 
+// The planner: one workgroup of THREADS threads builds the call's work plan in the workspace.
 template <int THREADS>
-__global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
+__device__ __forceinline__ void plan_body(const PlanParams& p) {
   constexpr int kPlanThreads = THREADS;
   constexpr int kPlanWaves = THREADS / 64;
   constexpr int kBucketsPerThread = kSortBuckets / THREADS;
@@ -614,6 +616,24 @@ __global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
   }
 }
 
+template <int THREADS>
+__global__ void __launch_bounds__(THREADS) plan_kernel(const PlanParams p) {
+  plan_body<THREADS>(p);
+}
+
+// The plan and this step's K/V write in one launch: workgroup 0 plans, the others scatter the new K/V rows.
+// They are independent (the planner reads only the metadata; only the attention kernel reads what the write
+// stores), and each alone is about one launch's fixed cost.
+template <int THREADS>
+__global__ void __launch_bounds__(THREADS) write_plan_kernel(const PlanParams p, const KvWriteParams w) {
+  if (blockIdx.x == 0) {
+    plan_body<THREADS>(p);
+    return;
+  }
+  kv_write_chunks(w, static_cast<int>(blockIdx.x - 1) * THREADS + static_cast<int>(threadIdx.x),
+                  static_cast<int>(gridDim.x - 1) * THREADS);
+}
+
 // bf16 NaN rows for the sequences a plan rejected (q_len > context, negative context, context past the table):
 // bad metadata shows in the result without a host check.  A sequence whose query range itself is inconsistent
 // owns no rows and is left alone.  Called by every thread of one workgroup (THREADS threads, whole waves); each
@@ -730,6 +750,20 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
   if (p.num_seqs > 128) hipLaunchKernelGGL(plan_kernel<256>, dim3(1), dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(plan_kernel<64>, dim3(1), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_plan(const PlanParams& p, const KvWriteParams& w, hipStream_t stream) {
+  if (w.num_tokens == 0) return launch_plan(p, stream);
+  const int threads = p.num_seqs > 128 ? 256 : 64;
+  // The write's workgroups cover at most kWriteGridLanes lanes, as in launch_kv_write (the host's bound on
+  // the chunk count leaves one such stride of room below 2^31).
+  const int64_t chunks = static_cast<int64_t>(w.num_tokens) * 2 * w.chunks_per_row;
+  int64_t blocks = (chunks + threads - 1) / threads;
+  if (blocks > kWriteGridLanes / threads) blocks = kWriteGridLanes / threads;
+  const dim3 grid(static_cast<unsigned>(1 + blocks));
+  if (threads == 256) hipLaunchKernelGGL(write_plan_kernel<256>, grid, dim3(256), 0, stream, p, w);
+  else hipLaunchKernelGGL(write_plan_kernel<64>, grid, dim3(64), 0, stream, p, w);
   return hipGetLastError();
 }
 

@@ -171,21 +171,18 @@ int scratch_address(void** addr) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int paged_kv_abi_version(void) { return kAbiVersion; }
-
-const char* paged_kv_last_error(void) { return g_error.c_str(); }
-
-int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int64_t num_tokens,
-                   void* k_cache, void* v_cache, int64_t num_blocks, int32_t block_size,
-                   int64_t block_stride, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                   void* stream) {
+// Checks paged_kv_write's arguments and fills *p (p->num_tokens == 0: nothing to write).  Launches nothing.
+int write_params(const void* k, const void* v, const int32_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                 void* v_cache, int64_t num_blocks, int32_t block_size, int64_t block_stride, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t dtype, pkv::KvWriteParams* p) {
   if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
   int64_t stride = 0;
   const int rc = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
   if (rc != PKV_OK) return rc;
-  if (num_tokens == 0) return succeed();
+  *p = pkv::KvWriteParams{};
+  if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return fail(PKV_ERR_INVALID_ARG, "null pointer among k, v, slot_mapping, k_cache, v_cache");
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -196,17 +193,36 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, in
   // The kernel strides over the 16-byte chunks with a 32-bit index: the last stride must not overflow.
   if (num_tokens > (int64_t{INT32_MAX} - pkv::kWriteGridLanes) / (2 * cpr))
     return fail(PKV_ERR_UNSUPPORTED, "num_tokens * row size too large for one call; split the write");
+  p->k = k;
+  p->v = v;
+  p->slot_mapping = slot_mapping;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  p->num_tokens = static_cast<int>(num_tokens);
+  p->chunks_per_row = static_cast<int>(cpr);
+  p->block_size_log2 = log2i(block_size);
+  p->num_slots = num_blocks * block_size;
+  p->block_stride_bytes = stride * elem_bytes(dtype);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_abi_version(void) { return kAbiVersion; }
+
+const char* paged_kv_last_error(void) { return g_error.c_str(); }
+
+int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int64_t num_tokens,
+                   void* k_cache, void* v_cache, int64_t num_blocks, int32_t block_size,
+                   int64_t block_stride, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   void* stream) {
   pkv::KvWriteParams p{};
-  p.k = k;
-  p.v = v;
-  p.slot_mapping = slot_mapping;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.num_tokens = static_cast<int>(num_tokens);
-  p.chunks_per_row = static_cast<int>(cpr);
-  p.block_size_log2 = log2i(block_size);
-  p.num_slots = num_blocks * block_size;
-  p.block_stride_bytes = stride * elem_bytes(dtype);
+  const int rc = write_params(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_blocks, block_size,
+                              block_stride, num_kv_heads, head_dim, dtype, &p);
+  if (rc != PKV_OK) return rc;
+  if (p.num_tokens == 0) return succeed();
   const hipError_t e = pkv::launch_kv_write(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("paged_kv_write launch", e);
   return succeed();
@@ -267,7 +283,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                    int64_t block_stride, float scale, int32_t dtype, int32_t max_q_len_hint,
                    const pkv::PrefixParams* prefix, void* workspace, size_t workspace_bytes, void* stream,
-                   bool noalloc = false, bool run_only = false) {
+                   bool noalloc = false, bool run_only = false, const pkv::KvWriteParams* fused_write = nullptr) {
   if (num_seqs < 0 || total_q < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs and total_q must be >= 0");
   int64_t stride = 0;
   const int rc = check_pool(dtype, head_dim, block_size, num_kv_heads, num_blocks, block_stride, &stride);
@@ -282,7 +298,15 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   const int group = num_q_heads / num_kv_heads;
   if (total_q * group > INT32_MAX / 2 || total_q * num_q_heads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "total_q too large for one call");
-  if (num_seqs == 0 || total_q == 0) return succeed();
+  // A K/V write to do first (fused_write): with the plan when there is one, else on its own.
+  const bool write_first = fused_write != nullptr && fused_write->num_tokens > 0;
+  if (num_seqs == 0 || total_q == 0) {
+    if (write_first) {
+      const hipError_t e = pkv::launch_kv_write(*fused_write, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail("paged_kv_write launch", e);
+    }
+    return succeed();
+  }
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return fail(PKV_ERR_INVALID_ARG,
                 "null pointer among out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc");
@@ -312,6 +336,10 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   const bool timed = g_ev_start != nullptr && g_ev_stop != nullptr;
 
   if (dtype == PKV_FP32) {
+    if (write_first) {
+      const hipError_t e = pkv::launch_kv_write(*fused_write, st);
+      if (e != hipSuccess) return hip_fail("paged_kv_write launch", e);
+    }
     if (timed) hipEventRecord(g_ev_start, st);
     hipError_t e = pkv::launch_attention_fp32(p, head_dim, st);
     if (e != hipSuccess) return hip_fail("fp32 attention launch", e);
@@ -405,7 +433,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
 
   hipError_t e = hipSuccess;
   if (!run_only) {
-    e = pkv::launch_plan(pp, st);
+    e = write_first ? pkv::launch_write_plan(pp, *fused_write, st) : pkv::launch_plan(pp, st);
     if (e != hipSuccess) return hip_fail("plan launch", e);
   }
   int64_t grid = grid_wgs;
@@ -436,6 +464,24 @@ int paged_attention_forward(void* out, const void* q, const void* k_cache, const
                         query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
                         num_blocks, block_stride, scale, dtype, max_q_len_hint, nullptr, workspace,
                         workspace_bytes, stream);
+}
+
+int paged_attention_write_forward(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                  int64_t num_tokens, void* out, const void* q, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                                  int64_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int64_t num_blocks, int64_t block_stride, float scale,
+                                  int32_t dtype, int32_t max_q_len_hint, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  pkv::KvWriteParams wp{};
+  const int rc = write_params(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, num_blocks, block_size,
+                              block_stride, num_kv_heads, head_dim, dtype, &wp);
+  if (rc != PKV_OK) return rc;
+  return attention_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks, block_stride, scale, dtype, max_q_len_hint, nullptr, workspace,
+                        workspace_bytes, stream, /*noalloc=*/false, /*run_only=*/false, &wp);
 }
 
 int paged_attention_run(void* out, const void* q, const void* k_cache, const void* v_cache,

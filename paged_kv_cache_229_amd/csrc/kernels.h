@@ -197,6 +197,8 @@ struct CopyBlocksParams {
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, int num_pairs, hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+// The plan and a K/V write (w.num_tokens may be 0) in one launch.
+hipError_t launch_write_plan(const PlanParams& p, const KvWriteParams& w, hipStream_t stream);
 // grid = persistent workgroups; each work item runs on the tile kind its unit carries, or (narrow_only) on the
 // 16-row body, for plans made with tile kind 1 throughout.
 hipError_t launch_attention(const AttnParams& p, int head_dim, bool narrow_only, int grid, hipStream_t stream);

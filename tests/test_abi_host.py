@@ -113,6 +113,35 @@ def test_forward_rejects(over, status):
     assert N.lib().paged_kv_last_error()
 
 
+def _write_fwd(**over):
+    """paged_attention_write_forward: _fwd's attention arguments plus a write of T_new tokens (pool shared)."""
+    a = dict(kn=FAKE, vn=FAKE, slot=FAKE, T_new=2, out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mbps=4, ctx=FAKE,
+             qsl=FAKE, N=2, T=3, hq=8, hkv=2, d=128, bs=16, nb=64, stride=0, scale=0.1, dtype=N.PKV_BF16, hint=-1,
+             ws=0, wsb=0)
+    a.update(over)
+    return N.lib().paged_attention_write_forward(
+        a["kn"], a["vn"], a["slot"], a["T_new"], a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mbps"], a["ctx"],
+        a["qsl"], a["N"], a["T"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["stride"], a["scale"], a["dtype"],
+        a["hint"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T_new=-1), N.PKV_ERR_INVALID_ARG),        # the write's own checks come first
+    (dict(kn=0), N.PKV_ERR_INVALID_ARG),
+    (dict(slot=FAKE + 2), N.PKV_ERR_INVALID_ARG),
+    (dict(vn=FAKE + 8), N.PKV_ERR_INVALID_ARG),
+    (dict(bs=24), N.PKV_ERR_UNSUPPORTED),           # pool checks: shared by both parts
+    (dict(scale=0.0), N.PKV_ERR_INVALID_ARG),       # then the attention's
+    (dict(hq=6, hkv=4), N.PKV_ERR_INVALID_ARG),
+    (dict(mbps=1 << 25), N.PKV_ERR_UNSUPPORTED),
+    (dict(ws=0, wsb=0), N.PKV_ERR_WORKSPACE),
+])
+def test_write_forward_rejects(over, status):
+    """Every error of either part is reported before anything is launched (no GPU here)."""
+    assert _write_fwd(**over) == status
+    assert N.lib().paged_kv_last_error()
+
+
 def test_forward_empty_is_noop():
     assert _fwd(N=0, out=0, q=0, kc=0, vc=0, bt=0, ctx=0, qsl=0) == N.PKV_OK
     assert _fwd(T=0, out=0, q=0) == N.PKV_OK

@@ -1,0 +1,92 @@
+"""paged_attention_write_forward: the step's K/V write and the attention in one call, the work plan made in the
+write's launch.  Pools and output must be bit-identical to paged_kv_write followed by paged_attention_forward
+(on a second copy of the same pools), and within tolerance of the oracle's write-then-attend step; also with
+no new tokens, with no query rows (the write alone), and in float32 (no plan)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_229_amd as pkv
+from gpu_util import check_close, log, out_f64, to_torch
+from workloads import BF16, FP32, build_workload, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _device(w, st):
+    return dict(q=to_torch(st.q, w.dtype), k_new=to_torch(st.k_new, w.dtype), v_new=to_torch(st.v_new, w.dtype),
+                slot_mapping=to_torch(st.slot_mapping, None), context_lens=to_torch(st.context_lens, None),
+                query_start_loc=to_torch(st.query_start_loc, None), block_tables=to_torch(w.block_tables, None),
+                max_q_len=int(np.max(np.diff(st.query_start_loc), initial=0)))
+
+
+def _both(w, st):
+    """(fused output, separate output, fused pools, separate pools) for step st on fresh pool copies."""
+    s = _device(w, st)
+    pools = [(to_torch(w.k_pool, w.dtype), to_torch(w.v_pool, w.dtype)) for _ in range(2)]
+    (kf, vf), (ks, vs) = pools
+    att = (s["block_tables"], s["context_lens"], s["query_start_loc"])
+    fused = pkv.paged_attention_write_forward(s["k_new"], s["v_new"], s["slot_mapping"], s["q"], kf, vf, *att,
+                                              scale=w.scale, max_q_len=s["max_q_len"])
+    pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], ks, vs)
+    sep = pkv.paged_attention_forward(s["q"], ks, vs, *att, scale=w.scale, max_q_len=s["max_q_len"])
+    torch.cuda.synchronize()
+    return fused, sep, (kf, vf), (ks, vs)
+
+
+def _assert_same(fused, sep, pf, ps, what):
+    assert torch.equal(pf[0], ps[0]) and torch.equal(pf[1], ps[1]), f"{what}: pools differ"
+    assert np.array_equal(out_f64(fused), out_f64(sep), equal_nan=True), f"{what}: outputs differ"
+
+
+@pytest.mark.parametrize("name", ["decode", "spec", "mixed", "prefix"])
+def test_same_as_write_then_forward(name):
+    w = make_config(name, "small")
+    log(f"write + forward in one call: small {name}")
+    fused, sep, pf, ps = _both(w, w.steps[0])
+    _assert_same(fused, sep, pf, ps, name)
+    _, _, ref = oracle.run_step(w.k_pool, w.v_pool, w.block_tables, w.steps[0], w.scale, w.dtype)
+    check_close(out_f64(fused), ref, w.dtype, f"{name} write_forward vs oracle")
+
+
+def test_float32():
+    w = build_workload(np.random.default_rng(71), name="wf32", dtype=FP32, num_q_heads=4, num_kv_heads=2,
+                       head_dim=64, block_size=16, q_lens=[1, 3, 2], context_lens=[50, 90, 17])
+    log("write + forward in one call: float32")
+    fused, sep, pf, ps = _both(w, w.steps[0])
+    _assert_same(fused, sep, pf, ps, "float32")
+    _, _, ref = oracle.run_step(w.k_pool, w.v_pool, w.block_tables, w.steps[0], w.scale, w.dtype)
+    check_close(out_f64(fused), ref, FP32, "float32 write_forward vs oracle")
+
+
+def test_no_new_tokens_and_no_query_rows():
+    """A write of zero tokens (the plan launches alone) and a call whose sequences have no query rows (the
+    write alone), each against the separate calls."""
+    w = build_workload(np.random.default_rng(73), name="wedge", dtype=BF16, num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, q_lens=[2, 1, 3], context_lens=[40, 70, 33])
+    st = w.steps[0]
+    log("write + forward in one call: no new tokens")
+    s = _device(w, st)
+    att = (s["block_tables"], s["context_lens"], s["query_start_loc"])
+    empty = s["k_new"][:0]
+    kf, vf = to_torch(w.k_pool, w.dtype), to_torch(w.v_pool, w.dtype)
+    ks, vs = to_torch(w.k_pool, w.dtype), to_torch(w.v_pool, w.dtype)
+    fused = pkv.paged_attention_write_forward(empty, empty, s["slot_mapping"][:0], s["q"], kf, vf, *att,
+                                              scale=w.scale)
+    sep = pkv.paged_attention_forward(s["q"], ks, vs, *att, scale=w.scale)
+    torch.cuda.synchronize()
+    _assert_same(fused, sep, (kf, vf), (ks, vs), "no new tokens")
+
+    log("write + forward in one call: no query rows")
+    no_rows = torch.zeros_like(s["query_start_loc"])
+    q0 = s["q"][:0]
+    kf, vf = to_torch(w.k_pool, w.dtype), to_torch(w.v_pool, w.dtype)
+    ks, vs = to_torch(w.k_pool, w.dtype), to_torch(w.v_pool, w.dtype)
+    pkv.paged_attention_write_forward(s["k_new"], s["v_new"], s["slot_mapping"], q0, kf, vf, s["block_tables"],
+                                      s["context_lens"], no_rows, scale=w.scale)
+    pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(kf, ks) and torch.equal(vf, vs), "no query rows: pools differ"
+    assert not torch.equal(kf, to_torch(w.k_pool, w.dtype)), "the write wrote nothing"
