@@ -1,7 +1,7 @@
 // Device-side work plan and split-context reduction for paged attention.
 //
 // The host never reads context_lens or query_start_loc (that would need a device-to-host sync), so the
-// decomposition into work is made here, on the device, by one workgroup (one wave up to 128 sequences):
+// decomposition into work is made here, on the device, by one workgroup (one wave up to 64 sequences and tiles):
 //
 //   unit = (sequence s, row tile t, context partition p), processed once per kv head.
 //
@@ -32,7 +32,8 @@
 namespace pkv {
 namespace {
 
-// One workgroup plans the whole call (one wave for up to 128 sequences, four waves beyond): every step is
+// One workgroup plans the whole call (one wave for up to 64 sequences and tiles, four waves beyond: each walk
+// over the sequences or tiles is then one round of memory loads per thread): every step is
 // a per-thread loop over sequences s = tid, tid + THREADS, ... followed by a reduction or scan (DPP
 // inside each wave, then the wave totals through LDS).  Each sequence's
 // (new tokens, context, tiles) is read from global memory once and kept in LDS (for the first
@@ -748,14 +749,14 @@ __global__ void __launch_bounds__(kThreads) split_reduce_kernel(const AttnParams
 }  // namespace
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
-  if (p.num_seqs > 128) hipLaunchKernelGGL(plan_kernel<256>, dim3(1), dim3(256), 0, stream, p);
+  if (plan_threads(p) == 256) hipLaunchKernelGGL(plan_kernel<256>, dim3(1), dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(plan_kernel<64>, dim3(1), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_write_plan(const PlanParams& p, const KvWriteParams& w, hipStream_t stream) {
   if (w.num_tokens == 0) return launch_plan(p, stream);
-  const int threads = p.num_seqs > 128 ? 256 : 64;
+  const int threads = plan_threads(p);
   // The write's workgroups cover at most kWriteGridLanes lanes, as in launch_kv_write (the host's bound on
   // the chunk count leaves one such stride of room below 2^31).
   const int64_t chunks = static_cast<int64_t>(w.num_tokens) * 2 * w.chunks_per_row;

@@ -4,6 +4,7 @@
 // can be exercised without a GPU.  Nothing here reads device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -427,6 +428,12 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   pp.unit_cap = static_cast<int>(w.unit_cap);
   pp.tile_cap = static_cast<int>(w.tile_cap);
   pp.prow_cap = static_cast<int>(w.prow_cap);
+  // Sequence s takes ceil(n_s G / 128) tiles at most: in all at most (total_q G + 127 num_seqs) / 128, and
+  // with the q-length hint at most num_seqs ceil(hint G / 128).
+  pp.tiles_bound = (total_q * group + 127 * static_cast<int64_t>(num_seqs)) / pkv::tile_rows_of(1);
+  if (max_q_len_hint > 0)
+    pp.tiles_bound = std::min<int64_t>(pp.tiles_bound, static_cast<int64_t>(num_seqs) *
+                                           ((static_cast<int64_t>(max_q_len_hint) * group + 127) / 128));
   if (prefix) pp.prefix = *prefix;
   pp.buf = b;
   for (int i = 0; i < 3; ++i) pp.sig[i] = p.sig[i];

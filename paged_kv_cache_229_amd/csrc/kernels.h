@@ -136,7 +136,15 @@ struct PlanParams {
   PrefixParams prefix;
   PlanBuffers buf;
   int sig[3];  // call-shape signature, written to the header words kHdrSig0..2
+  // Upper bound on the row tiles (the host's, from total_q, the group and the q-length hint): with more
+  // sequences or tiles than one wave's 64 lanes, the planner runs on four waves, so that each of its walks
+  // over the sequences and tiles is one round of memory loads rather than several.
+  int64_t tiles_bound;
 };
+// Threads of the planner's workgroup.
+inline int plan_threads(const PlanParams& p) {
+  return p.num_seqs > 64 || p.tiles_bound > 64 ? 256 : 64;
+}
 
 struct AttnParams {
   void* out;
