@@ -323,17 +323,17 @@ def test_single_long_decode_keeps_the_grid_busy():
     check_close(out_f64(out), outs[0], BF16, "single long decode")
 
 
-@pytest.mark.parametrize("block_size", [16, 32])
-def test_late_pieces(block_size):
+@pytest.mark.parametrize("block_size,head_dim", [(16, 128), (32, 128), (16, 64)])
+def test_late_pieces(block_size, head_dim):
     """Long partitions (a small item target gives P of about 4900 keys) over contexts that end off any stage
     boundary: each split tile's last keys become late pieces (more units than whole partitions of P give),
     which must start on stage boundaries like every other partition; checked against the oracle with
     multi-token queries."""
     ctx = [9001, 12345, 17003, 10477, 15555, 13131]
-    w = build_workload(np.random.default_rng(47 + block_size), name="late", dtype=BF16, num_q_heads=8,
-                       num_kv_heads=2, head_dim=128, block_size=block_size, q_lens=[1, 4, 8, 3, 1, 6],
+    w = build_workload(np.random.default_rng(47 + block_size + head_dim), name="late", dtype=BF16, num_q_heads=8,
+                       num_kv_heads=2, head_dim=head_dim, block_size=block_size, q_lens=[1, 4, 8, 3, 1, 6],
                        context_lens=ctx)
-    log(f"late pieces, block size {block_size}")
+    log(f"late pieces, block size {block_size}, head dim {head_dim}")
     pkv.set_tuning(0, 32, 0)
     dw = DeviceWorkload(w)
     st = dw.steps[0]
@@ -350,7 +350,7 @@ def test_late_pieces(block_size):
     whole = sum(-(-int(c) // partition) for c in st["context_lens"].cpu().numpy())
     assert partition >= 4096 and units > whole, (partition, units, whole)
     _, _, outs = _oracle_steps(w)
-    check_close(out_f64(out), outs[0], BF16, f"late pieces, block size {block_size}")
+    check_close(out_f64(out), outs[0], BF16, f"late pieces, block size {block_size}, head dim {head_dim}")
 
 
 def test_empty_and_degenerate():
