@@ -412,6 +412,10 @@ def main() -> None:
         print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
+    if args.fused and (args.prefix_pass or args.plan_reuse or args.graph):
+        print("bench.py: --fused times plain steps through paged_attention_write_forward; it does not combine "
+              "with --prefix-pass, --plan-reuse or --graph", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -440,10 +444,6 @@ def main() -> None:
           flush=True)
     if args.prefix_pass and w.shared_prefix_blocks == 0:
         print("bench.py: --prefix-pass needs a workload with shared prefix blocks (prefix)", file=sys.stderr)
-        sys.exit(2)
-    if args.fused and (args.prefix_pass or args.plan_reuse or args.graph):
-        print("bench.py: --fused times plain steps through paged_attention_write_forward; it does not combine "
-              "with --prefix-pass, --plan-reuse or --graph", file=sys.stderr)
         sys.exit(2)
     work = algorithmic_work(w)
     traffic_key = w.name if args.subset == "all" else f"{w.name}:{args.subset}"

@@ -1,5 +1,6 @@
-"""bench.py's command-line contract on the host: more than one GPU is refused with a message and a non-zero
-exit before any GPU work, and the counter record it reads matches the kernel sources it covers."""
+"""bench.py's command-line contract on the host: more than one GPU, and flag combinations it does not time,
+are refused with a message and a non-zero exit before any GPU work, and the counter record it reads matches the
+kernel sources it covers."""
 
 import json
 import os
@@ -14,6 +15,16 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_fused_with_plan_reuse_is_refused():
+    """--fused times plain steps through one call; combined with the layer-reuse mode it is refused before any
+    GPU work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--fused", "--plan-reuse"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--fused" in r.stderr
     assert r.stdout.strip() == ""
 
 
