@@ -1,7 +1,8 @@
 """paged_attention_write_forward: the step's K/V write and the attention in one call, the work plan made in the
 write's launch.  Pools and output must be bit-identical to paged_kv_write followed by paged_attention_forward
 (on a second copy of the same pools), and within tolerance of the oracle's write-then-attend step; also with
-no new tokens, with no query rows (the write alone), and in float32 (no plan)."""
+no new tokens, with no query rows (the write alone), in float32 (no plan), and as the first layer of a step
+whose other layers run on its plan."""
 
 import numpy as np
 import pytest
@@ -90,3 +91,31 @@ def test_no_new_tokens_and_no_query_rows():
     torch.cuda.synchronize()
     assert torch.equal(kf, ks) and torch.equal(vf, vs), "no query rows: pools differ"
     assert not torch.equal(kf, to_torch(w.k_pool, w.dtype)), "the write wrote nothing"
+
+
+def test_later_layers_run_on_its_plan():
+    """A model step: paged_attention_write_forward for the first layer, then paged_kv_write + paged_attention_run
+    for the others (each layer its own pools): every layer bit-identical to a fresh write + forward."""
+    w = make_config("spec", "small")
+    st = w.steps[0]
+    s = _device(w, st)
+    att = (s["block_tables"], s["context_lens"], s["query_start_loc"])
+    need = pkv.workspace_size(w.num_seqs, s["q"].shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim,
+                              s["q"].dtype, s["max_q_len"])
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=s["q"].device)
+    log("write_forward plans the first layer, the others run on its plan")
+    for layer in range(3):
+        kp = torch.roll(to_torch(w.k_pool, w.dtype), layer, dims=0)
+        vp = torch.roll(to_torch(w.v_pool, w.dtype), 2 * layer, dims=0)
+        kf, vf, ks, vs = kp.clone(), vp.clone(), kp.clone(), vp.clone()
+        if layer == 0:
+            got = pkv.paged_attention_write_forward(s["k_new"], s["v_new"], s["slot_mapping"], s["q"], kf, vf, *att,
+                                                    scale=w.scale, workspace=ws, max_q_len=s["max_q_len"])
+        else:
+            pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], kf, vf)
+            got = pkv.paged_attention_run(s["q"], kf, vf, *att, scale=w.scale, workspace=ws,
+                                          max_q_len=s["max_q_len"])
+        pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], ks, vs)
+        ref = pkv.paged_attention_forward(s["q"], ks, vs, *att, scale=w.scale, max_q_len=s["max_q_len"])
+        torch.cuda.synchronize()
+        _assert_same(got, ref, (kf, vf), (ks, vs), f"layer {layer}")
