@@ -50,6 +50,26 @@ def gpu_case(draw, dtype: str):
 
 
 @st.composite
+def long_case(draw, dtype: str):
+    """Few sequences over long contexts (3 K - 9 K keys) with decode-like and speculative q_lens (small row
+    tiles), at the supported geometry: with a small work-item target the partitions are long and every split
+    tile ends on late pieces."""
+    group = draw(st.sampled_from([1, 2, 4, 8]))
+    hkv = draw(st.sampled_from([1, 2]))
+    bs = draw(st.sampled_from([16, 32]))
+    d = draw(st.sampled_from([64, 128]))
+    q_lens, ctx, shared = draw(lengths(4, 9000, st.integers(1, 8), 2, bs))
+    ctx = [max(c, 3000 + n) for c, n in zip(ctx, q_lens)]
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    w = build_workload(np.random.default_rng(seed), name="property-long", dtype=dtype, num_q_heads=group * hkv,
+                       num_kv_heads=hkv, head_dim=d, block_size=bs, q_lens=q_lens, context_lens=ctx,
+                       shared_prefix_blocks=shared)
+    w.description = (f"seed={seed} G={group} Hkv={hkv} D={d} bs={bs} shared={shared} "
+                     f"q_lens={q_lens} ctx={ctx}")
+    return w
+
+
+@st.composite
 def tiny_case(draw, dtype: str):
     """Tiny geometry for scalar brute force: head_dim 2..8, block sizes 1..8, contexts up to 30."""
     group = draw(st.sampled_from([1, 2, 3, 4]))

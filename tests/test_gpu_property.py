@@ -1,9 +1,10 @@
 """Property tier on the GPU: random cases at the supported geometry (query groups {1, 2, 4, 8, 32}, block
 sizes {16, 32}, head_dim {64, 128}, q_len from 0 to chunk size, random block permutations, shared first
 blocks) through write + attention, against the oracle, under both bf16 row-tile kinds with automatic or
-short forced partitions, and on the float32 path.  A fixed number of derandomised examples without
-shrinking: reproducible, and the first failure ends the test."""
+short forced partitions, on the float32 path, and over long contexts with long partitions (late pieces).  A
+fixed number of derandomised examples without shrinking: reproducible, and the first failure ends the test."""
 
+import numpy as np
 import pytest
 import torch
 from hypothesis import HealthCheck, Phase, given, settings
@@ -12,7 +13,7 @@ from hypothesis import strategies as st
 import oracle
 import paged_kv_cache_229_amd as pkv
 from gpu_util import DeviceWorkload, check_close, log, out_f64
-from property_cases import gpu_case
+from property_cases import gpu_case, long_case
 from workloads import BF16, FP32
 
 pytestmark = pytest.mark.gpu
@@ -48,3 +49,44 @@ def test_property_bf16(w, kind, partition):
 @given(gpu_case(FP32))
 def test_property_fp32(w):
     _run(w, 0, 0)
+
+
+@_settings(16)
+@given(long_case(BF16), st.sampled_from([2, 3, 4, 8]))
+def test_property_late_pieces(w, items):
+    """A small work-item target over long contexts: partitions of thousands of keys, so split tiles end on
+    late pieces, in random geometries."""
+    log(f"property case target_items={items}: {w.description}")
+    pkv.set_tuning(0, items, 0)
+    try:
+        dw = DeviceWorkload(w)
+        s = dw.steps[0]
+        ws = torch.zeros(max(256, pkv.workspace_size(w.num_seqs, s["q"].shape[0], w.num_q_heads, w.num_kv_heads,
+                                                     w.head_dim, s["q"].dtype, s["max_q_len"])),
+                         dtype=torch.uint8, device=s["q"].device)
+        pkv.paged_kv_write(s["k_new"], s["v_new"], s["slot_mapping"], dw.k_pool, dw.v_pool)
+        out = pkv.paged_attention_forward(s["q"], dw.k_pool, dw.v_pool, dw.block_tables, s["context_lens"],
+                                          s["query_start_loc"], scale=w.scale, workspace=ws,
+                                          max_q_len=s["max_q_len"])
+        torch.cuda.synchronize()
+    finally:
+        pkv.set_tuning(0, 0, 0)
+    # The plan's unit count is the documented rule's: one small tile per sequence here (at most 64 rows);
+    # with partitions P of 2048 keys or more, a tile longer than P ends on late pieces of max(P/4, 1024) keys
+    # over its last 15%, after bulk partitions of P over the first whole stages of the rest.
+    hdr = ws[:64].cpu().numpy().view(np.int32)
+    units, partition = int(hdr[0]), int(hdr[2])
+    expect, late = 0, 0
+    for c in (int(c) for c in w.steps[0].context_lens):
+        if partition >= 2048 and c > partition:
+            bulk = (c - c * 3 // 20) // 64 * 64
+            piece = max(partition // 4 // 64 * 64, 1024)
+            n_late = -(-(c - bulk) // piece)
+            expect += -(-bulk // partition) + n_late
+            late += n_late
+        else:
+            expect += -(-c // partition)
+    assert units == expect, (units, expect, partition)
+    log(f"  partition {partition}, units {units}, of which {late} late pieces")
+    _, _, ref = oracle.run_step(w.k_pool, w.v_pool, w.block_tables, w.steps[0], w.scale, w.dtype)
+    check_close(out_f64(out), ref, w.dtype, f"property late pieces, target {items}")
