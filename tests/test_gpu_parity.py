@@ -323,6 +323,24 @@ def test_single_long_decode_keeps_the_grid_busy():
     check_close(out_f64(out), outs[0], BF16, "single long decode")
 
 
+@pytest.mark.parametrize("n_seqs,max_q", [(64, 1), (65, 1), (100, 3), (128, 2), (40, 40)])
+def test_planner_width(n_seqs, max_q):
+    """The planner runs on one wave for at most 64 sequences and row tiles, on four beyond: batches on both
+    sides of that bound (65-128 short sequences, and 40 sequences whose queries take about 100 tiles) against
+    the oracle."""
+    rng = np.random.default_rng(1000 + n_seqs + max_q)
+    q_lens = rng.integers(1, max_q + 1, n_seqs)
+    ctx = q_lens + rng.integers(0, 400, n_seqs)
+    w = build_workload(rng, name="width", dtype=BF16, num_q_heads=16, num_kv_heads=2, head_dim=64,
+                       block_size=16, q_lens=q_lens, context_lens=ctx)
+    log(f"planner width: {n_seqs} sequences, q_len <= {max_q}")
+    dw = DeviceWorkload(w)
+    out = dw.run_step(0)
+    torch.cuda.synchronize()
+    _, _, outs = _oracle_steps(w)
+    check_close(out_f64(out), outs[0], BF16, f"{n_seqs} sequences, q_len <= {max_q}")
+
+
 @pytest.mark.parametrize("block_size,head_dim", [(16, 128), (32, 128), (16, 64)])
 def test_late_pieces(block_size, head_dim):
     """Long partitions (a small item target gives P of about 4900 keys) over contexts that end off any stage
