@@ -61,12 +61,13 @@ struct Geo {
   static constexpr int ROWB = 2 * D;         // bytes of one key row in LDS
   static constexpr int TILEB = kStageKeys * ROWB;
   static constexpr int STAGEB = 2 * TILEB;   // K tile + V tile
-  static constexpr int NBUF = 4;
+  static constexpr int NBUF = 4;  // ring_slot() orders exactly four slots
   static constexpr int LDS = NBUF * STAGEB;
   static constexpr int MERGE_SLOT = DT * 256 + 32;  // floats per (wave, n-tile) in the merge buffer
   static constexpr int MERGE_BYTES = NW * NTW * MERGE_SLOT * 4;
   static constexpr int SMEM = LDS > MERGE_BYTES ? LDS : MERGE_BYTES;  // ring, later reused for the merge
   static_assert(NL >= 1 && KPW % KPL == 0, "stage split");
+  static_assert((STAGEB & (STAGEB - 1)) == 0, "a slot base is whole bits above every offset inside a slot");
 };
 
 // One work item (unit, kv head g) on 16-row waves.  Every thread of the workgroup calls it; `smem` is the
@@ -102,8 +103,10 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
   const int tr_key = 4 * g4 + (l16 >> 2);
   const int tr_half = (l16 & 1) << 3;       // byte offset inside the 16-byte chunk
   const int tr_chunk = (l16 & 3) >> 1;      // chunk offset inside the 16-channel tile
-  // Byte offsets of the lane's fragment reads inside a stage, for key group 0; other key groups (+16,
-  // +32, +48 keys) add a constant, because the swizzle depends on the key modulo 16 only.
+  // Byte offsets of the lane's fragment reads in the ring, for key group 0; other key groups (+16, +32,
+  // +48 keys) add a constant, because the swizzle depends on the key modulo 16 only.  They include the
+  // current stage's slot: stage st sits in slot ring_slot(st) (0, 1, 3, 2), so one XOR per register moves
+  // them on to the next stage.
   int koff[T::DC];  // K: key l16, 16-byte chunk 4*dc + g4 (A operand of S^T = K Q^T)
   int voff[T::DT];  // V: transpose-read row of tile dt (A operand of O^T += V^T P^T)
 #pragma unroll
@@ -157,11 +160,11 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
         phys[i] = tbl[kfirst >> bs_log2];
       }
     };
-    // Wave w fetches keys [KPW*w, KPW*(w+1)) of stage st into ring slot st % NBUF.  Keys at or past ke are
+    // Wave w fetches keys [KPW*w, KPW*(w+1)) of stage st into ring slot ring_slot(st).  Keys at or past ke are
     // clamped to row ke-1 of the same block (a wave-wide load never spans two blocks); their scores are
     // masked, so those rows carry probability 0, and rows past the context are never read.
     auto issue = [&](int st, const int* phys) {
-      unsigned char* const kdst = smem + (st & (T::NBUF - 1)) * T::STAGEB;
+      unsigned char* const kdst = smem + ring_slot(st) * T::STAGEB;
       const int key0 = kb + st * kStageKeys + T::KPW * wave;
 #pragma unroll
       for (int i = 0; i < T::NL; ++i) {
@@ -321,13 +324,12 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
       __syncthreads();  // all waves' loads of stage st landed; all waves done with stage st-1
       if (st + 3 < nst) issue(st + 3, tbn);
 
-      const unsigned char* const stage = smem + (st & (T::NBUF - 1)) * T::STAGEB;
       const unsigned char* kp[T::DC];
       const unsigned char* vp[T::DT];
 #pragma unroll
-      for (int dc = 0; dc < T::DC; ++dc) kp[dc] = stage + koff[dc];
+      for (int dc = 0; dc < T::DC; ++dc) kp[dc] = smem + koff[dc];
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) vp[dt] = stage + voff[dt];
+      for (int dt = 0; dt < T::DT; ++dt) vp[dt] = smem + voff[dt];
       const int kstage = kb + st * kStageKeys;
       // Two 32-key chunks per stage; chunk number st*2+c goes to the key-group (st*2+c) % WK.
 #pragma unroll
@@ -338,6 +340,12 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
         else if (ntv > 0) chunk(std::integral_constant<int, 1>{}, kp, vp, c, kc0);
       }
       if (st + 4 < nst) fetch_table(st + 4, tbn);
+      // On to the next stage's slot: ring_slot(st) ^ ring_slot(st + 1) is bit 0 for even st, bit 1 for odd.
+      const int flip = (st & 1) ? 2 * T::STAGEB : T::STAGEB;
+#pragma unroll
+      for (int dc = 0; dc < T::DC; ++dc) koff[dc] ^= flip;
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) voff[dt] ^= flip;
     }
 
     // (workgroup w's first item was item w: the queue hands out the items from gridDim.x on)

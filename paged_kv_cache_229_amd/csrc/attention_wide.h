@@ -67,7 +67,7 @@ struct WideGeo {
   static constexpr int ROWB = 2 * D;            // bytes of one key row in LDS
   static constexpr int TILEB = kStageKeys * ROWB;
   static constexpr int STAGEB = 2 * TILEB;      // K tile + V tile
-  static constexpr int NBUF = 4;
+  static constexpr int NBUF = 4;                // ring_slot() orders exactly four slots
   static constexpr int RING = NBUF * STAGEB;
   // Merge slot of one wave, in floats: acc of its halves as [half][dt][j/4][lane][4], then (m, l) of
   // its rows.
@@ -76,6 +76,7 @@ struct WideGeo {
   static constexpr int MERGE_BYTES = NW * MSLOT * 4;
   static constexpr int SMEM = RING > MERGE_BYTES ? RING : MERGE_BYTES;
   static_assert(NL >= 1 && KPW % KPL == 0, "stage split");
+  static_assert((STAGEB & (STAGEB - 1)) == 0, "a slot base is whole bits above every offset inside a slot");
 };
 
 // One work item (unit, kv head g) on 32-row waves.  Every thread of the workgroup calls it; `smem` is the
@@ -109,10 +110,13 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
   const float inv_sl2 = 1.f / sl2;
   const unsigned lds_ring = static_cast<unsigned>(reinterpret_cast<size_t>((LDS_AS unsigned char*)smem));
 
-  // Lane offsets of the fragment reads inside a stage slot.  K (A operand of S^T): key l32, 16-byte chunk
+  // Lane offsets of the fragment reads in the ring.  K (A operand of S^T): key l32, 16-byte chunk
   // 2ks + hf.  V (A operand of O^T, transpose reads): in each 16-lane group, lane i points at key
   // 4hf + i/4 (+8 for the second read of a step) and channels 32dt + 16(group % 2) + 4(i % 4).  Later key
-  // groups (+16, +32) are constant offsets: the swizzle depends on the key modulo 16 only.
+  // groups (+16, +32) are constant offsets: the swizzle depends on the key modulo 16 only.  The offsets
+  // include the current stage's slot: stage st sits in slot gray(st mod 4) (0, 1, 3, 2), so consecutive
+  // stages' slots differ in one bit and one XOR per register moves every offset on to the next stage
+  // (a slot base added per read would cost two instructions per register and chunk).
   int kof[T::KS];
 #pragma unroll
   for (int ks = 0; ks < T::KS; ++ks) kof[ks] = l32 * T::ROWB + (((2 * ks + hf) ^ wide_swizzle<D>(l32)) << 4);
@@ -178,12 +182,12 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
         phys[i] = tbl[kfirst >> bs_log2];
       }
     };
-    // Wave w copies keys [KPW*w, KPW*(w+1)) of stage st into ring slot st % NBUF; keys at or past ke are
+    // Wave w copies keys [KPW*w, KPW*(w+1)) of stage st into ring slot ring_slot(st); keys at or past ke are
     // clamped to row ke-1 of the same block and masked.  Row-split items (long chunks: the tiles of one
     // sequence re-read its K/V) copy with the default cache policy, key-split ones stream non-temporally.
     auto issue_p = [&](int st, const int* phys, auto keep_tag) __attribute__((always_inline)) {
       constexpr bool KEEP = decltype(keep_tag)::value;
-      unsigned char* const kdst = smem + (st & (T::NBUF - 1)) * T::STAGEB;
+      unsigned char* const kdst = smem + ring_slot(st) * T::STAGEB;
       const int key0 = kb + st * kStageKeys + T::KPW * wave;
 #pragma unroll
       for (int i = 0; i < T::NL; ++i) {
@@ -262,7 +266,7 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
 
     // One 32-key chunk (keys kc0 + [0, 32) at rows 32c .. 32c+31 of the stage tiles) for every half of
     // the wave (a half without rows computes on zero queries; its results are never written).
-    auto chunk = [&](const unsigned char* slot, int c, int kc0) __attribute__((always_inline)) {
+    auto chunk = [&](int c, int kc0) __attribute__((always_inline)) {
       f32x16 sc[NH];
 #pragma unroll
       for (int h = 0; h < NH; ++h)
@@ -270,7 +274,7 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
         for (int j = 0; j < 16; ++j) sc[h][j] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(slot + kof[ks] + 32 * c * T::ROWB));
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(smem + kof[ks] + 32 * c * T::ROWB));
 #pragma unroll
         for (int h = 0; h < NH; ++h) sc[h] = mfma32(kf, q[h][ks], sc[h]);
       }
@@ -281,8 +285,8 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int ko = (32 * c + 16 * s2) * T::ROWB;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(slot + vof[dt][0] + ko));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(slot + vof[dt][1] + ko));
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(smem + vof[dt][0] + ko));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(smem + vof[dt][1] + ko));
           vf[dt][s2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       float sv[NH][16];
@@ -350,14 +354,22 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
       else wait_vmem<0>();
       __syncthreads();  // all waves' loads of stage st landed; all waves done with stage st-1
       if (st + 3 < nst) issue(st + 3, tbn);
-      const unsigned char* const slot = smem + (st & (T::NBUF - 1)) * T::STAGEB;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int kc0 = kb + st * kStageKeys + 32 * c;
         if (((st * 2 + c) % WK) != wk || kc0 > limw) continue;
-        if (nh > 0) chunk(slot, c, kc0);
+        if (nh > 0) chunk(c, kc0);
       }
       if (st + 4 < nst) fetch_table(st + 4, tbn);
+      // On to the next stage's slot: gray(st) ^ gray(st + 1) is slot bit 0 for even st, bit 1 for odd.
+      const int flip = (st & 1) ? 2 * T::STAGEB : T::STAGEB;
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) kof[ks] ^= flip;
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        vof[dt][0] ^= flip;
+        vof[dt][1] ^= flip;
+      }
     }
 
     // (workgroup w's first item was item w: the queue hands out the items from gridDim.x on)

@@ -22,6 +22,13 @@ __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, 
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Slot of stage st in a four-slot LDS ring: the Gray code of st mod 4 (0, 1, 3, 2), so that the slots of
+// consecutive stages differ in one bit.
+__device__ __forceinline__ int ring_slot(int st) {
+  const int r = st & 3;
+  return r ^ (r >> 1);
+}
+
 // D[m][n] += sum_k A[m][k] B[k][n] over a 16x16x32 tile; lane l holds A[l%16][8(l/16) + 0..7],
 // B[8(l/16) + 0..7][l%16] and D[4(l/16) + 0..3][l%16].
 __device__ inline f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
