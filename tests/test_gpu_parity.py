@@ -119,6 +119,26 @@ def test_tile_kinds(name, partition, kind):
     check_close(out_f64(out), outs[0], BF16, f"{name} kind={kind} P={partition}")
 
 
+@pytest.mark.parametrize("kind", [1, 2])
+@pytest.mark.parametrize("head_dim,block_size", [(128, 16), (64, 32)])
+def test_every_ring_phase(head_dim, block_size, kind):
+    """Whole items (one 1024-key partition each) of 1 to 9, 13 and 14 stages of 64 keys: the last stage falls
+    on every slot of the four-slot ring, and the long items wrap it several times; exact and ragged ends,
+    one or three query tokens per sequence; against the oracle."""
+    pkv.set_tuning(1024, 0, kind)
+    stages = list(range(1, 10)) + [13, 14]
+    ctx = [64 * s for s in stages] + [64 * s - 37 for s in stages]
+    q_lens = [1 + 2 * (i % 2) for i in range(len(ctx))]
+    w = build_workload(np.random.default_rng(4100 + head_dim + kind), name="ring", dtype=BF16, num_q_heads=8,
+                       num_kv_heads=2, head_dim=head_dim, block_size=block_size, q_lens=q_lens, context_lens=ctx)
+    log(f"ring phases D={head_dim} bs={block_size} tile_kind={kind}")
+    dw = DeviceWorkload(w)
+    out = dw.run_step(0)
+    _, _, outs = _oracle_steps(w)
+    torch.cuda.synchronize()
+    check_close(out_f64(out), outs[0], BF16, f"ring phases D{head_dim} kind={kind}")
+
+
 @pytest.mark.parametrize("dtype,kind", [(BF16, 1), (BF16, 2), (FP32, 0)])  # the float32 path has no row tiles
 @pytest.mark.parametrize("head_dim,block_size,hq,hkv", [(64, 8, 8, 2), (64, 32, 4, 4), (128, 64, 16, 1),
                                                          (128, 256, 6, 3)])
