@@ -353,12 +353,13 @@ __device__ __forceinline__ void wide_item(const AttnParams& p, const PlanWords& 
       else if (later == 1) wait_vmem<2 * T::NL>();
       else wait_vmem<0>();
       __syncthreads();  // all waves' loads of stage st landed; all waves done with stage st-1
-      if (st + 3 < nst) issue(st + 3, tbn);
+      // Stage st + 3 refills the slot of stage st - 1, free since the barrier.  Its copies are issued between
+      // the two chunks, so that each wave's first MFMAs follow the barrier directly.
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int kc0 = kb + st * kStageKeys + 32 * c;
-        if (((st * 2 + c) % WK) != wk || kc0 > limw) continue;
-        if (nh > 0) chunk(c, kc0);
+        if (((st * 2 + c) % WK) == wk && kc0 <= limw && nh > 0) chunk(c, kc0);
+        if (c == 0 && st + 3 < nst) issue(st + 3, tbn);
       }
       if (st + 4 < nst) fetch_table(st + 4, tbn);
       // On to the next stage's slot: gray(st) ^ gray(st + 1) is slot bit 0 for even st, bit 1 for odd.
