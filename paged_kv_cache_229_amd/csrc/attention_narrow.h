@@ -322,7 +322,6 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
       else if (later == 1) wait_vmem<2 * T::NL>();
       else wait_vmem<0>();
       __syncthreads();  // all waves' loads of stage st landed; all waves done with stage st-1
-      if (st + 3 < nst) issue(st + 3, tbn);
 
       const unsigned char* kp[T::DC];
       const unsigned char* vp[T::DT];
@@ -335,9 +334,11 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int kc0 = kstage + 32 * c;
-        if (((st * 2 + c) % WK) != wk || kc0 > limw) continue;
-        if (NTW > 1 && ntv == NTW) chunk(std::integral_constant<int, NTW>{}, kp, vp, c, kc0);
-        else if (ntv > 0) chunk(std::integral_constant<int, 1>{}, kp, vp, c, kc0);
+        if (((st * 2 + c) % WK) == wk && kc0 <= limw) {
+          if (NTW > 1 && ntv == NTW) chunk(std::integral_constant<int, NTW>{}, kp, vp, c, kc0);
+          else if (ntv > 0) chunk(std::integral_constant<int, 1>{}, kp, vp, c, kc0);
+        }
+        if (c == 0 && st + 3 < nst) issue(st + 3, tbn);
       }
       if (st + 4 < nst) fetch_table(st + 4, tbn);
       // On to the next stage's slot: ring_slot(st) ^ ring_slot(st + 1) is bit 0 for even st, bit 1 for odd.
