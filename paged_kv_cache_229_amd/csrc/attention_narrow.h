@@ -330,7 +330,9 @@ __device__ __forceinline__ void narrow_item(const AttnParams& p, const PlanWords
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) vp[dt] = smem + voff[dt];
       const int kstage = kb + st * kStageKeys;
-      // Two 32-key chunks per stage; chunk number st*2+c goes to the key-group (st*2+c) % WK.
+      // Two 32-key chunks per stage; chunk number st*2+c goes to the key-group (st*2+c) % WK.  The copy of
+      // stage st + 3 refills the slot of stage st - 1, free since the barrier; it goes out after the first
+      // chunk, so that the waves computing that chunk start right after the barrier.
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int kc0 = kstage + 32 * c;
